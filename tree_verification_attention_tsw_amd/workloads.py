@@ -1,0 +1,173 @@
+"""Seeded synthetic inputs for tree-verification attention.
+
+This module only produces inputs: tree topologies, Q/K/V tensors and index
+lists.  It holds none of the attention arithmetic, so both the GPU path and
+the float64 oracle can be fed from it.
+
+Shapes follow the workloads the TokenSwift pages talk about: 1.5B-14B models
+with MHA and GQA layouts, caches of about 100K tokens, a 3-ary candidate tree
+("From Hours to Minutes ..." arxivlens summary, Technical Contribution), and a
+draft pass that sees only a partial KV cache which always keeps the initial
+positions ("TokenSwift - A framework for accelerating ..." aiboss88 page,
+technical principles, dynamic KV cache update).  No dataset is involved: all
+values are N(0, 1) draws from torch generators with fixed seeds.
+"""
+from dataclasses import dataclass, field
+from typing import Optional, Tuple
+
+import numpy as np
+import torch
+
+F32 = "f32"
+BF16 = "bf16"
+
+# Four fixed head-dim channels of K are scaled by 8 in the long-context GQA
+# workload, standing in for the outlier channels real K caches show.  Scaling
+# by a power of two is exact in bfloat16.
+OUTLIER_CHANNELS = (0, 32, 64, 96)
+OUTLIER_SCALE = 8.0
+
+
+def kary_tree_parent(n_nodes: int, arity: int = 3) -> np.ndarray:
+    """Full k-ary tree numbered breadth-first: parent[i] = (i - 1) // k."""
+    p = np.empty(n_nodes, dtype=np.int32)
+    p[0] = -1
+    for i in range(1, n_nodes):
+        p[i] = (i - 1) // arity
+    return p
+
+
+def full_kary_nodes(depth: int, arity: int = 3) -> int:
+    """Node count of a full k-ary tree with `depth` levels below the root."""
+    return sum(arity ** lv for lv in range(depth + 1))
+
+
+def chain_parent(n_nodes: int) -> np.ndarray:
+    """A single path: node i's parent is i - 1."""
+    p = np.arange(-1, n_nodes - 1, dtype=np.int32)
+    return p
+
+
+def random_tree_parent(n_nodes: int, seed: int) -> np.ndarray:
+    """A random valid tree: root 0, every later node picks an earlier parent."""
+    rng = np.random.default_rng(seed)
+    p = np.empty(n_nodes, dtype=np.int32)
+    p[0] = -1
+    for i in range(1, n_nodes):
+        p[i] = rng.integers(0, i)
+    return p
+
+
+def retained_index_set(n_prefix: int, n_idx: int, n_keep: int, seed: int) -> np.ndarray:
+    """Sorted distinct positions: 0..n_keep-1 always, plus n_idx - n_keep drawn
+    uniformly without replacement from [n_keep, n_prefix)."""
+    n_keep = min(n_keep, n_idx, n_prefix)
+    rest = n_idx - n_keep
+    rng = np.random.default_rng(seed)
+    if rest > 0:
+        picks = rng.choice(np.arange(n_keep, n_prefix, dtype=np.int64), size=rest, replace=False)
+    else:
+        picks = np.zeros(0, dtype=np.int64)
+    idx = np.concatenate([np.arange(n_keep, dtype=np.int64), np.sort(picks)])
+    return idx.astype(np.int32)
+
+
+@dataclass
+class Workload:
+    """One attention call's shape and input recipe."""
+    name: str
+    Hq: int
+    Hkv: int
+    d: int
+    n_prefix: int
+    n_nodes: int
+    dtype: str
+    seed: int
+    tree: str = "ternary"          # "ternary" | "chain"
+    outliers: bool = False
+    n_idx: Optional[int] = None    # partial-KV variant when set
+    n_keep: int = 128
+    layers: int = 1
+    notes: str = field(default="")
+
+    @property
+    def G(self) -> int:
+        return self.Hq // self.Hkv
+
+    def parent(self) -> np.ndarray:
+        if self.tree == "chain":
+            return chain_parent(self.n_nodes)
+        return kary_tree_parent(self.n_nodes, 3)
+
+    @property
+    def cap(self) -> int:
+        return self.n_prefix + self.n_nodes
+
+    def scale(self) -> float:
+        return 1.0 / float(np.sqrt(self.d))
+
+    def kv_bytes(self) -> int:
+        """K+V bytes one layer-call must read (prefix or index set, plus tree rows)."""
+        esz = 4 if self.dtype == F32 else 2
+        keys = (self.n_idx if self.n_idx is not None else self.n_prefix) + self.n_nodes
+        return 2 * self.Hkv * keys * self.d * esz
+
+
+WORKLOADS = {
+    "tiny_mha_f32": Workload("tiny_mha_f32", Hq=4, Hkv=4, d=64, n_prefix=512,
+                             n_nodes=full_kary_nodes(2), dtype=F32, seed=1000),
+    "gqa8b_8k": Workload("gqa8b_8k", Hq=32, Hkv=8, d=128, n_prefix=8192,
+                         n_nodes=full_kary_nodes(3), dtype=BF16, seed=2000),
+    "gqa8b_100k": Workload("gqa8b_100k", Hq=32, Hkv=8, d=128, n_prefix=102400,
+                           n_nodes=full_kary_nodes(3), dtype=BF16, seed=3000, outliers=True),
+    "mha7b_100k": Workload("mha7b_100k", Hq=32, Hkv=32, d=128, n_prefix=102400,
+                           n_nodes=full_kary_nodes(3), dtype=BF16, seed=4000),
+    "gqa14b_100k": Workload("gqa14b_100k", Hq=40, Hkv=8, d=128, n_prefix=102400,
+                            n_nodes=full_kary_nodes(3), dtype=BF16, seed=5000),
+    "partial32_gqa8b_100k": Workload("partial32_gqa8b_100k", Hq=32, Hkv=8, d=128,
+                                     n_prefix=102400, n_nodes=4, dtype=BF16, seed=6000,
+                                     tree="chain", n_idx=4096, n_keep=128, layers=32),
+}
+
+
+def torch_dtype(dtype: str):
+    return torch.float32 if dtype == F32 else torch.bfloat16
+
+
+def make_qkv(w: Workload, layer: int = 0, device="cpu", seed_offset: int = 0
+             ) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+    """Q [T, Hq, d] and K, V [Hkv, n_prefix + T, d] for one layer.
+
+    Values are N(0, 1) float32 draws from a torch generator on `device`
+    seeded with seed + 7919 * layer + seed_offset, then rounded to bfloat16
+    (round-to-nearest-even) for bf16 workloads.  The same seed on a different
+    device gives different (but equally valid) values, so callers must hand
+    the oracle the exact tensors they used.
+    """
+    gen = torch.Generator(device=device)
+    gen.manual_seed(int(w.seed + 7919 * layer + seed_offset))
+    dt = torch_dtype(w.dtype)
+    q = torch.randn((w.n_nodes, w.Hq, w.d), generator=gen, device=device, dtype=torch.float32).to(dt)
+    k = torch.randn((w.Hkv, w.cap, w.d), generator=gen, device=device, dtype=torch.float32).to(dt)
+    v = torch.randn((w.Hkv, w.cap, w.d), generator=gen, device=device, dtype=torch.float32).to(dt)
+    if w.outliers:
+        for ch in OUTLIER_CHANNELS:
+            k[:, :, ch] *= OUTLIER_SCALE
+    return q, k, v
+
+
+def make_index_set(w: Workload, layer: int = 0) -> Optional[np.ndarray]:
+    if w.n_idx is None:
+        return None
+    return retained_index_set(w.n_prefix, w.n_idx, w.n_keep, w.seed + 104729 * (layer + 1))
+
+
+def oracle_view(t: torch.Tensor) -> np.ndarray:
+    """Host numpy view of an input tensor in the form the oracle takes:
+    float32 as is, bfloat16 as its raw uint16 bit patterns."""
+    t = t.detach().to("cpu").contiguous()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    if t.dtype == torch.float32:
+        return t.numpy()
+    raise TypeError(t.dtype)
