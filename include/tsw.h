@@ -1,0 +1,159 @@
+/*
+ * tsw.h -- C ABI of the tree-verification attention library for AMD MI355X
+ * (gfx950).
+ *
+ * The operation.  In TokenSwift's generation loop the drafted candidate
+ * tokens form a token tree (a simple 3-ary tree) and are verified in one
+ * forward pass with tree-structured attention against the full KV cache;
+ * the result must equal what the target model computes for each candidate
+ * on its own (lossless).  The draft pass runs the same model over a partial
+ * KV cache that always keeps the initial positions and a selection of later
+ * ones.  Sources:
+ *   - "TokenSwift - A framework for accelerating the generation of ultra-long
+ *     text" (aiboss88 project page), technical principles: tree-based
+ *     multi-candidate verification; dynamic KV cache update.
+ *   - "90分钟生成10万Token，新框架实现3倍无损加速超长文本生成" (Tencent Cloud
+ *     article), 技术原理 figure text (verification with the full KV cache,
+ *     tree-based attention) and 优势与特点 / 无损的输出质量 (the draft model is
+ *     the target model with a partial KV cache).
+ *   - "From Hours to Minutes: Lossless Acceleration of Ultra Long Sequence
+ *     Generation up to 100K Tokens" (arxivlens summary), Technical
+ *     Contribution: 3-ary tree, KV compression.
+ *
+ * For tree node i (0 <= i < T) and query head h, with kv head g = h / (Hq/Hkv):
+ *   visible(i) = prefix  u  { n_prefix + j : j is i or an ancestor of i }
+ *   prefix     = {0 .. n_prefix-1}                  (tsw_tree_attn_verify)
+ *              = {idx[0] .. idx[n_idx-1]}           (tsw_tree_attn_partial)
+ *   s_p        = scale * dot(Q[i][h][:], K[g][p][:])        p in visible(i)
+ *   O[i][h][:] = sum_p exp(s_p) V[g][p][:] / sum_p exp(s_p)
+ *   LSE[i][h]  = ln(sum_p exp(s_p))
+ * The tree's own K/V rows are stored in the cache right after the committed
+ * prefix: node j at position n_prefix + j.
+ *
+ * Memory layout (all row-major, element type per desc->dtype):
+ *   q    [T][Hq][d]                       device, contiguous
+ *   k, v [Hkv][rows][d]                   device, kv_head_stride elements
+ *                                         between heads, rows >= n_prefix + T
+ *   o    [T][Hq][d]   float32             device
+ *   lse  [T][Hq]      float32             device, natural log
+ *   parent [T] int32                      HOST memory; parent[0] = -1 and
+ *                                         0 <= parent[i] < i for i >= 1
+ *   idx  [n_idx] int32                    device; sorted ascending, distinct,
+ *                                         every entry in [0, n_prefix)
+ *
+ * Ownership and errors.  The caller owns every buffer.  The library never
+ * allocates or frees memory and never synchronises: compute calls enqueue
+ * kernels on `stream` and return.  Host arguments (desc, parent) are read
+ * before the call returns.  Device buffers must stay valid until the stream
+ * work completes; o/lse/workspace must not overlap the inputs or each other.
+ * All argument checks run before any HIP call; on an error nothing is
+ * launched and the outputs are untouched.  idx validity is a precondition
+ * (it lives on the device and is not inspected); violating it gives
+ * unspecified results but no out-of-bounds access as long as every entry is
+ * in [0, n_prefix).  Functions return TSW_OK (0) or a negative status.
+ */
+#ifndef TSW_H
+#define TSW_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+    TSW_OK = 0,
+    TSW_EINVAL = -1,       /* null pointer, bad size, stride, scale or reserved field */
+    TSW_EBADTREE = -2,     /* parent[] is not a tree rooted at node 0 in topological order */
+    TSW_EBADINDEX = -3,    /* n_idx < 0 or n_idx > n_prefix */
+    TSW_EUNSUPPORTED = -4, /* head dim, dtype or implementation choice not supported */
+    TSW_ENOSPACE = -5,     /* workspace smaller than tsw_workspace_size() */
+    TSW_EHIP = -6          /* a HIP runtime call failed (no device, launch failure) */
+};
+
+enum { TSW_DTYPE_F32 = 0, TSW_DTYPE_BF16 = 1 };
+
+/* Kernel family choice.  AUTO takes the matrix-core (MFMA) kernel for
+ * bfloat16 with d = 128 and shapes it covers, else the vector-ALU kernel. */
+enum { TSW_IMPL_AUTO = 0, TSW_IMPL_VALU = 1, TSW_IMPL_MFMA = 2 };
+
+/* A cache stream handle: a hipStream_t (NULL = the legacy default stream). */
+typedef void* tsw_stream_t;
+
+typedef struct tsw_attn_desc {
+    int32_t T;              /* tree nodes (query tokens), 1..64 */
+    int32_t Hq;             /* query heads, >= 1 */
+    int32_t Hkv;            /* kv heads, >= 1, Hq % Hkv == 0 */
+    int32_t d;              /* head dim: 64 or 128 */
+    int64_t n_prefix;       /* committed cache positions, >= 0 */
+    int64_t kv_head_stride; /* elements between kv heads in k and v, >= (n_prefix + T) * d */
+    int32_t dtype;          /* TSW_DTYPE_F32 or TSW_DTYPE_BF16, for q, k and v */
+    int32_t impl;           /* TSW_IMPL_* */
+    float scale;            /* score scale, positive and finite (1/sqrt(d) usually) */
+    int32_t reserved;       /* must be 0 */
+} tsw_attn_desc;
+
+/* Builds the tree mask on the host: bit j of mask[i] is set iff node j is
+ * node i or an ancestor of i; depth[i] = edges from the root (may be NULL).
+ * parent, mask, depth are host arrays of length T, 1 <= T <= 64.
+ * Errors: TSW_EINVAL (null pointer, T out of range), TSW_EBADTREE. */
+int tsw_tree_mask_build(const int32_t* parent, int32_t T, uint64_t* mask, int32_t* depth);
+
+/* Number of KV splits the library uses for this problem on the current
+ * device (the split-K degree of tsw_tree_attn_verify / _partial).  n_idx < 0
+ * selects the verify variant.  Needs a HIP device (queries its CU count). */
+int tsw_plan_splits(const tsw_attn_desc* desc, int64_t n_idx, int32_t* n_splits);
+
+/* Workspace bytes tsw_tree_attn_verify (n_idx < 0) or tsw_tree_attn_partial
+ * (n_idx >= 0) need on the current device: the per-split partial results
+ * n_splits * T * Hq * (d + 1) float32 plus alignment. */
+int tsw_workspace_size(const tsw_attn_desc* desc, int64_t n_idx, size_t* bytes);
+
+/* Tree verification against the full cache: O and LSE for every (node,
+ * query head).  workspace: device memory of at least tsw_workspace_size()
+ * bytes, 256-byte aligned, contents need not be initialised. */
+int tsw_tree_attn_verify(const tsw_attn_desc* desc, const void* q, const void* k, const void* v,
+                         const int32_t* parent, float* o, float* lse, void* workspace,
+                         size_t workspace_bytes, tsw_stream_t stream);
+
+/* Draft-pass variant: the prefix is the index list idx[0..n_idx) (device
+ * memory, sorted, distinct, < n_prefix) instead of all committed positions;
+ * the tree rows are attended under the tree mask as in verify.  n_idx = 0
+ * attends to the tree rows only. */
+int tsw_tree_attn_partial(const tsw_attn_desc* desc, const void* q, const void* k, const void* v,
+                          const int32_t* parent, const int32_t* idx, int64_t n_idx, float* o,
+                          float* lse, void* workspace, size_t workspace_bytes,
+                          tsw_stream_t stream);
+
+/* First phase on its own: split the prefix key list (all positions when
+ * idx == NULL, else idx[0..n_idx)) into n_splits contiguous parts and write,
+ * for every part s and row (node, head), the attention result over that part
+ * normalised within the part, and its LSE:
+ *   part_o   [n_splits][T][Hq][d] float32 (device)
+ *   part_lse [n_splits][T][Hq]    float32 (device), -inf when the part holds
+ *                                 no visible key for the row.
+ * The last part also holds the tree rows.  n_splits >= 1; parts may be
+ * empty.  Combining the parts with tsw_lse_merge gives the verify / partial
+ * result; the same merge combines parts computed on different devices. */
+int tsw_tree_attn_split(const tsw_attn_desc* desc, const void* q, const void* k, const void* v,
+                        const int32_t* parent, const int32_t* idx, int64_t n_idx,
+                        int32_t n_splits, float* part_o, float* part_lse, tsw_stream_t stream);
+
+/* Second phase: merge n_splits partial attention results over disjoint key
+ * sets into the result over their union:
+ *   LSE = ln(sum_s exp(L_s)),  O = sum_s exp(L_s - LSE) O_s
+ * part_o [n_splits][n_rows][d], part_lse [n_splits][n_rows] (natural log,
+ * -inf for empty parts), o [n_rows][d], lse [n_rows]; all float32 device
+ * memory.  Rows whose parts are all empty get O = 0 and LSE = -inf. */
+int tsw_lse_merge(int32_t n_splits, int64_t n_rows, int32_t d, const float* part_o,
+                  const float* part_lse, float* o, float* lse, tsw_stream_t stream);
+
+/* Static description of a status code. */
+const char* tsw_status_str(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TSW_H */

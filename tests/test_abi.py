@@ -1,0 +1,155 @@
+"""The C-ABI library without a GPU: it loads, exports every function the
+public header declares, builds tree masks bit-exactly, and rejects bad
+arguments with the documented status codes before touching HIP."""
+import ctypes
+
+import numpy as np
+import pytest
+
+import oracle
+import tree_verification_attention_tsw_amd as tsw
+from tree_verification_attention_tsw_amd import workloads as wl
+from tree_verification_attention_tsw_amd import build as tsw_build
+
+TSW_OK, EINVAL, EBADTREE, EBADINDEX, EUNSUP, ENOSPACE, EHIP = 0, -1, -2, -3, -4, -5, -6
+FAKE = ctypes.c_void_p(0x10000)   # never dereferenced: argument checks run first
+
+
+@pytest.fixture(scope="module")
+def L():
+    if tsw_build.stale():
+        tsw_build.build()
+    return tsw.lib()
+
+
+def test_exports_every_declared_symbol(L):
+    names = tsw.declared_functions()
+    assert len(names) >= 8
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_status_strings(L):
+    for s in (TSW_OK, EINVAL, EBADTREE, EBADINDEX, EUNSUP, ENOSPACE, EHIP):
+        assert tsw.status_str(s)
+    assert tsw.status_str(-99) == "unknown status"
+
+
+@pytest.mark.parametrize("T", [1, 2, 13, 40, 63, 64])
+def test_mask_ternary_matches_oracle(L, T):
+    parent = wl.kary_tree_parent(T, 3)
+    m1, d1 = tsw.tree_mask(parent)
+    m2, d2 = oracle.mask_build(parent)
+    assert np.array_equal(m1, m2) and np.array_equal(d1, d2)
+
+
+def test_mask_random_and_chain_match_oracle(L):
+    for seed in range(50):
+        T = 1 + (seed * 7) % 64
+        for parent in (wl.random_tree_parent(T, seed), wl.chain_parent(T)):
+            m1, d1 = tsw.tree_mask(parent)
+            m2, d2 = oracle.mask_build(parent)
+            assert np.array_equal(m1, m2) and np.array_equal(d1, d2)
+
+
+def test_mask_closed_form_totals(L):
+    for n, total in ((13, 34), (40, 142)):
+        m, _ = tsw.tree_mask(wl.kary_tree_parent(n, 3))
+        assert sum(bin(int(x)).count("1") for x in m) == total
+
+
+@pytest.mark.parametrize("parent,code", [
+    ([0], EBADTREE), ([-1, 1], EBADTREE), ([-1, 0, 3], EBADTREE), ([-1, -1], EBADTREE),
+    ([-1, 0, 0, 2, 5], EBADTREE)])
+def test_mask_rejects_bad_trees(L, parent, code):
+    p = np.array(parent, dtype=np.int32)
+    mask = np.zeros(64, dtype=np.uint64)
+    assert L.tsw_tree_mask_build(p.ctypes.data_as(ctypes.c_void_p), len(parent),
+                                 mask.ctypes.data_as(ctypes.c_void_p), None) == code
+
+
+def test_mask_rejects_sizes(L):
+    p = np.full(65, 0, dtype=np.int32)
+    p[0] = -1
+    mask = np.zeros(65, dtype=np.uint64)
+    args = (p.ctypes.data_as(ctypes.c_void_p), None, mask.ctypes.data_as(ctypes.c_void_p), None)
+    assert L.tsw_tree_mask_build(args[0], 0, args[2], None) == EINVAL
+    assert L.tsw_tree_mask_build(args[0], 65, args[2], None) == EINVAL
+    assert L.tsw_tree_mask_build(None, 3, args[2], None) == EINVAL
+    assert L.tsw_tree_mask_build(args[0], 3, None, None) == EINVAL
+
+
+def _desc(**kw):
+    d = tsw.AttnDesc()
+    d.T, d.Hq, d.Hkv, d.d = 13, 4, 2, 128
+    d.n_prefix = 100
+    d.kv_head_stride = (100 + 13) * 128
+    d.dtype = tsw.DTYPE_BF16
+    d.impl = 0
+    d.scale = 0.088
+    d.reserved = 0
+    for k, v in kw.items():
+        setattr(d, k, v)
+    return d
+
+
+PARENT = np.ascontiguousarray(wl.kary_tree_parent(13, 3))
+
+
+def _verify(L, desc, parent=PARENT, q=FAKE, o=FAKE, ws=FAKE):
+    return L.tsw_tree_attn_verify(ctypes.byref(desc), q, FAKE, FAKE,
+                                  parent.ctypes.data_as(ctypes.c_void_p), o, FAKE, ws, 1 << 30, None)
+
+
+@pytest.mark.parametrize("field,value,code", [
+    ("T", 0, EINVAL), ("T", 65, EINVAL), ("Hq", 3, EINVAL), ("Hkv", 0, EINVAL),
+    ("d", 96, EUNSUP), ("dtype", 7, EUNSUP), ("impl", 9, EUNSUP), ("reserved", 1, EINVAL),
+    ("scale", 0.0, EINVAL), ("scale", -1.0, EINVAL), ("scale", float("nan"), EINVAL),
+    ("scale", float("inf"), EINVAL), ("n_prefix", -1, EINVAL),
+    ("kv_head_stride", (100 + 13) * 128 - 1, EINVAL)])
+def test_desc_errors(L, field, value, code):
+    assert _verify(L, _desc(**{field: value})) == code
+
+
+def test_mfma_forced_on_unsupported_shape(L):
+    # float32 inputs have no matrix-core kernel here
+    assert _verify(L, _desc(impl=2, dtype=tsw.DTYPE_F32)) == EUNSUP
+    # more than 16 query blocks of 16 rows per kv head
+    assert _verify(L, _desc(impl=2, T=64, Hq=40, Hkv=8, d=128,
+                            kv_head_stride=(100 + 64) * 128),
+                   parent=np.ascontiguousarray(wl.kary_tree_parent(64, 3))) == EUNSUP
+
+
+def test_null_pointers_and_bad_tree(L):
+    d = _desc()
+    assert _verify(L, d, q=None) == EINVAL
+    assert _verify(L, d, o=None) == EINVAL
+    bad = np.array([-1, 0, 5] + [0] * 10, dtype=np.int32)
+    assert _verify(L, d, parent=bad) == EBADTREE
+
+
+def test_partial_index_errors(L):
+    d = _desc()
+    p = PARENT.ctypes.data_as(ctypes.c_void_p)
+    call = lambda n: L.tsw_tree_attn_partial(ctypes.byref(d), FAKE, FAKE, FAKE, p, FAKE, n,
+                                             FAKE, FAKE, FAKE, 1 << 30, None)
+    assert call(-1) == EBADINDEX
+    assert call(101) == EBADINDEX
+
+
+def test_split_and_merge_argument_errors(L):
+    d = _desc()
+    p = PARENT.ctypes.data_as(ctypes.c_void_p)
+    assert L.tsw_tree_attn_split(ctypes.byref(d), FAKE, FAKE, FAKE, p, None, 0, 0, FAKE, FAKE,
+                                 None) == EINVAL
+    assert L.tsw_tree_attn_split(ctypes.byref(d), FAKE, FAKE, FAKE, p, FAKE, 101, 4, FAKE,
+                                 FAKE, None) == EBADINDEX
+    assert L.tsw_lse_merge(0, 10, 128, FAKE, FAKE, FAKE, FAKE, None) == EINVAL
+    assert L.tsw_lse_merge(2, -1, 128, FAKE, FAKE, FAKE, FAKE, None) == EINVAL
+    assert L.tsw_lse_merge(2, 10, 128, None, FAKE, FAKE, FAKE, None) == EINVAL
+    # zero rows is a no-op that needs no device
+    assert L.tsw_lse_merge(2, 0, 128, None, None, None, None, None) == TSW_OK
+
+
+def test_null_workspace(L):
+    assert _verify(L, _desc(), ws=None) == EINVAL

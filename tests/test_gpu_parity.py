@@ -1,0 +1,336 @@
+"""GPU parity: the HIP path (through the C ABI) against the float64 oracle on
+identical seeded inputs.  Tolerances: max-abs 1e-5 on O and LSE for float32
+inputs, 4e-3 for bfloat16 inputs with float32 accumulation; tree masks are
+compared bit-exactly.  Large workloads are checked on sampled (node, head)
+rows that the oracle computes one by one, plus properties on every row."""
+import os
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import tree_verification_attention_tsw_amd as tsw
+from tree_verification_attention_tsw_amd import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-5, "bf16": 4e-3}
+NTHREADS = min(16, len(os.sched_getaffinity(0)))
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    tsw.lib()
+    return torch.device("cuda:0")
+
+
+def gen(shape, seed, dtype, device="cuda"):
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    return torch.randn(shape, generator=g, device=device, dtype=torch.float32).to(dtype)
+
+
+def check(o, lse, o_ref, lse_ref, tol, what):
+    o = o.detach().cpu().double().numpy()
+    lse = lse.detach().cpu().double().numpy()
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse)), what + ": non-finite output"
+    eo = float(np.max(np.abs(o - o_ref)))
+    el = float(np.max(np.abs(lse - lse_ref)))
+    say("%s: max|dO| %.3g max|dLSE| %.3g" % (what, eo, el))
+    assert eo <= tol and el <= tol, (what, eo, el)
+
+
+def run_case(T, Hq, Hkv, d, n_prefix, dtype, parent, idx=None, impl="auto", seed=0,
+             cap_extra=0, head_pad=0, rows=None, k_override=None):
+    """Generate inputs, run the GPU path, compare with the oracle."""
+    tdt = torch.float32 if dtype == "f32" else torch.bfloat16
+    cap = n_prefix + T + cap_extra
+    q = gen((T, Hq, d), seed + 1, tdt)
+    kb = gen((Hkv, cap + head_pad, d), seed + 2, tdt)
+    vb = gen((Hkv, cap + head_pad, d), seed + 3, tdt)
+    if k_override is not None:
+        kb = k_override(kb)
+    k, v = kb[:, :cap], vb[:, :cap]
+    say("case T=%d Hq=%d Hkv=%d d=%d n_prefix=%d %s idx=%s impl=%s" % (
+        T, Hq, Hkv, d, n_prefix, dtype, None if idx is None else len(idx), impl))
+    if idx is None:
+        o, lse = tsw.tree_attn_verify(q, k, v, parent, n_prefix, impl=impl)
+    else:
+        it = torch.from_numpy(np.asarray(idx, dtype=np.int32)).to(q.device)
+        o, lse = tsw.tree_attn_partial(q, k, v, parent, it, n_prefix, impl=impl)
+    torch.cuda.synchronize()
+    qn, kn, vn = wl.oracle_view(q), wl.oracle_view(k.contiguous()), wl.oracle_view(v.contiguous())
+    o_ref, lse_ref = oracle.tree_attn(qn, kn, vn, parent, n_prefix, 1.0 / np.sqrt(d), idx=idx,
+                                      rows=rows, nthreads=NTHREADS)
+    if rows is not None:
+        o_s = o.reshape(T * Hq, d)[torch.as_tensor(rows, device=o.device).long()]
+        l_s = lse.reshape(T * Hq)[torch.as_tensor(rows, device=o.device).long()]
+        check(o_s, l_s, o_ref, lse_ref, TOL[dtype], "sampled rows")
+    else:
+        check(o, lse, o_ref, lse_ref, TOL[dtype], "all rows")
+    return q, k, v, o, lse
+
+
+# ------------------------------------------------------------ the workloads
+
+def test_workload_tiny_mha_f32():
+    w = wl.WORKLOADS["tiny_mha_f32"]
+    q, k, v = wl.make_qkv(w, device="cuda")
+    for impl in ("auto", "valu"):
+        o, lse = tsw.tree_attn_verify(q, k, v, w.parent(), w.n_prefix, impl=impl)
+        torch.cuda.synchronize()
+        o_ref, l_ref = oracle.tree_attn(wl.oracle_view(q), wl.oracle_view(k), wl.oracle_view(v),
+                                        w.parent(), w.n_prefix, w.scale(), nthreads=NTHREADS)
+        check(o, lse, o_ref, l_ref, TOL["f32"], "tiny %s" % impl)
+
+
+@pytest.mark.parametrize("impl", ["auto", "valu"])
+def test_workload_gqa8b_8k(impl):
+    w = wl.WORKLOADS["gqa8b_8k"]
+    q, k, v = wl.make_qkv(w, device="cuda")
+    o, lse = tsw.tree_attn_verify(q, k, v, w.parent(), w.n_prefix, impl=impl)
+    torch.cuda.synchronize()
+    o_ref, l_ref = oracle.tree_attn(wl.oracle_view(q), wl.oracle_view(k), wl.oracle_view(v),
+                                    w.parent(), w.n_prefix, w.scale(), nthreads=NTHREADS)
+    check(o, lse, o_ref, l_ref, TOL["bf16"], "gqa8b_8k %s" % impl)
+
+
+def _sample_rows(T, Hq, n, seed):
+    rng = np.random.default_rng(seed)
+    fixed = [t * Hq + 0 for t in range(T)] + [t * Hq + (Hq - 1) for t in (0, T - 1)]
+    extra = rng.choice(T * Hq, size=n, replace=False).tolist()
+    return np.array(sorted(set(fixed + extra)), dtype=np.int32)
+
+
+@pytest.mark.parametrize("name", ["gqa8b_100k", "mha7b_100k", "gqa14b_100k"])
+def test_workload_100k_sampled(name):
+    w = wl.WORKLOADS[name]
+    q, k, v = wl.make_qkv(w, device="cuda")
+    o, lse = tsw.tree_attn_verify(q, k, v, w.parent(), w.n_prefix)
+    torch.cuda.synchronize()
+    rows = _sample_rows(w.n_nodes, w.Hq, 24, w.seed)
+    o_ref, l_ref = oracle.tree_attn(wl.oracle_view(q), wl.oracle_view(k), wl.oracle_view(v),
+                                    w.parent(), w.n_prefix, w.scale(), rows=rows,
+                                    nthreads=NTHREADS)
+    ri = torch.as_tensor(rows, device=o.device).long()
+    check(o.reshape(-1, w.d)[ri], lse.reshape(-1)[ri], o_ref, l_ref, TOL["bf16"], name)
+    # every row: finite, and the LSE of a node can only grow with its depth
+    # (its visible set is a superset of its parent's) -- up to tolerance.
+    assert torch.isfinite(o).all() and torch.isfinite(lse).all()
+    par = w.parent()
+    l_all = lse.cpu().double().numpy()
+    for t in range(1, w.n_nodes):
+        assert np.all(l_all[t] >= l_all[par[t]] - 2 * TOL["bf16"])
+
+
+def test_workload_partial32_layers():
+    w = wl.WORKLOADS["partial32_gqa8b_100k"]
+    for layer in (0, 13, 31):
+        q, k, v = wl.make_qkv(w, layer=layer, device="cuda")
+        idx = wl.make_index_set(w, layer)
+        assert len(idx) == 4096 and list(idx[:128]) == list(range(128))
+        assert np.all(np.diff(idx) > 0) and idx[-1] < w.n_prefix
+        it = torch.from_numpy(idx).to(q.device)
+        o, lse = tsw.tree_attn_partial(q, k, v, w.parent(), it, w.n_prefix)
+        torch.cuda.synchronize()
+        o_ref, l_ref = oracle.tree_attn(wl.oracle_view(q), wl.oracle_view(k), wl.oracle_view(v),
+                                        w.parent(), w.n_prefix, w.scale(), idx=idx,
+                                        nthreads=NTHREADS)
+        check(o, lse, o_ref, l_ref, TOL["bf16"], "partial layer %d" % layer)
+        del q, k, v
+        torch.cuda.empty_cache()
+
+
+# ------------------------------------------------------------ shapes / edges
+
+# Query rows per kv head M = T * G select the matrix-core shape (blocks of 16
+# rows: 1-2, 3-4, 5-8, 9-12, 13-16); each shape is covered, with ragged M.
+MFMA_SHAPES = [
+    (1, 1, 1), (13, 1, 1), (16, 2, 1), (4, 8, 8), (40, 1, 1), (13, 4, 1), (40, 2, 1),
+    (33, 4, 1), (40, 4, 1), (47, 4, 1), (64, 3, 1), (40, 5, 1), (64, 4, 1), (61, 4, 1),
+]
+
+
+@pytest.mark.parametrize("T,G,Hkv", MFMA_SHAPES)
+def test_mfma_shapes(T, G, Hkv):
+    run_case(T, G * Hkv, Hkv, 128, 1000 + 37, "bf16", wl.random_tree_parent(T, T * G),
+             impl="mfma", seed=T * 100 + G)
+
+
+@pytest.mark.parametrize("n_prefix", [0, 1, 31, 32, 63, 64, 65, 127, 129, 255, 4097])
+def test_ragged_prefix(n_prefix):
+    run_case(40, 8, 2, 128, n_prefix, "bf16", wl.kary_tree_parent(40, 3), seed=n_prefix)
+
+
+@pytest.mark.parametrize("T", [1, 2, 3, 17, 63, 64])
+def test_tree_sizes(T):
+    run_case(T, 4, 1, 128, 777, "bf16", wl.random_tree_parent(T, T), seed=7 * T)
+
+
+def test_chain_tree():
+    run_case(64, 4, 2, 128, 513, "bf16", wl.chain_parent(64), seed=11)
+
+
+@pytest.mark.parametrize("dtype,d,impl", [("f32", 64, "auto"), ("f32", 128, "auto"),
+                                          ("bf16", 64, "auto"), ("bf16", 128, "valu")])
+def test_valu_kernel(dtype, d, impl):
+    run_case(13, 8, 2, d, 700, dtype, wl.kary_tree_parent(13, 3), impl=impl, seed=d)
+    run_case(40, 4, 4, d, 300, dtype, wl.random_tree_parent(40, 3), impl=impl, seed=d + 1)
+
+
+def test_head_stride_padding():
+    run_case(13, 8, 4, 128, 2000, "bf16", wl.kary_tree_parent(13, 3), head_pad=333, seed=5)
+    run_case(13, 4, 4, 64, 500, "f32", wl.kary_tree_parent(13, 3), head_pad=17, seed=6)
+
+
+def test_rows_beyond_cache_are_not_read():
+    # cache rows past n_prefix + T are poisoned; they must not leak
+    run_case(13, 8, 2, 128, 900, "bf16", wl.kary_tree_parent(13, 3), cap_extra=100, seed=8,
+             k_override=lambda kb: kb.index_fill_(1, torch.arange(900 + 13, kb.shape[1],
+                                                                  device=kb.device), float("nan")))
+
+
+@pytest.mark.parametrize("n_idx", [0, 1, 100, 4096, 5000])
+def test_partial_sizes(n_idx):
+    npre = 20000
+    idx = wl.retained_index_set(npre, n_idx, min(128, n_idx), n_idx)
+    run_case(4, 32, 8, 128, npre, "bf16", wl.chain_parent(4), idx=idx, seed=n_idx)
+    run_case(13, 8, 2, 128, npre, "bf16", wl.kary_tree_parent(13, 3), idx=idx, seed=n_idx + 1)
+
+
+def test_partial_valu_and_f32():
+    npre = 3000
+    idx = wl.retained_index_set(npre, 700, 64, 3)
+    run_case(4, 8, 2, 128, npre, "bf16", wl.chain_parent(4), idx=idx, impl="valu", seed=21)
+    run_case(13, 4, 4, 64, npre, "f32", wl.kary_tree_parent(13, 3), idx=idx, seed=22)
+
+
+def test_partial_all_positions_equals_verify():
+    T, Hq, Hkv, d, npre = 40, 32, 8, 128, 6000
+    q = gen((T, Hq, d), 31, torch.bfloat16)
+    k = gen((Hkv, npre + T, d), 32, torch.bfloat16)
+    v = gen((Hkv, npre + T, d), 33, torch.bfloat16)
+    parent = wl.kary_tree_parent(T, 3)
+    o1, l1 = tsw.tree_attn_verify(q, k, v, parent, npre)
+    idx = torch.arange(npre, dtype=torch.int32, device=q.device)
+    o2, l2 = tsw.tree_attn_partial(q, k, v, parent, idx, npre)
+    torch.cuda.synchronize()
+    assert float((o1 - o2).abs().max()) <= 1e-5
+    assert float((l1 - l2).abs().max()) <= 1e-5
+
+
+def test_partial_unselected_rows_poisoned():
+    """Rows outside the index list hold NaN: the result stays finite and
+    matches the oracle (which never reads them)."""
+    T, Hq, Hkv, d, npre = 4, 32, 8, 128, 30000
+    idx = wl.retained_index_set(npre, 4096, 128, 99)
+    sel = np.zeros(npre + T, dtype=bool)
+    sel[idx] = True
+    sel[npre:] = True
+    bad = torch.from_numpy(np.nonzero(~sel)[0]).cuda()
+    q = gen((T, Hq, d), 41, torch.bfloat16)
+    k = gen((Hkv, npre + T, d), 42, torch.bfloat16).index_fill_(1, bad, float("nan"))
+    v = gen((Hkv, npre + T, d), 43, torch.bfloat16).index_fill_(1, bad, float("nan"))
+    parent = wl.chain_parent(T)
+    o, lse = tsw.tree_attn_partial(q, k, v, parent, torch.from_numpy(idx).cuda(), npre)
+    torch.cuda.synchronize()
+    o_ref, l_ref = oracle.tree_attn(wl.oracle_view(q), wl.oracle_view(k), wl.oracle_view(v),
+                                    parent, npre, 1 / np.sqrt(d), idx=idx, nthreads=NTHREADS)
+    check(o, lse, o_ref, l_ref, TOL["bf16"], "poisoned partial")
+
+
+def test_non_ancestor_tree_rows_do_not_leak():
+    """Tree rows that are not ancestors get a huge key along the query
+    direction: the output must not change."""
+    T, Hq, Hkv, d, npre = 40, 8, 2, 128, 2000
+    parent = wl.kary_tree_parent(T, 3)
+    q = gen((T, Hq, d), 51, torch.bfloat16)
+    k = gen((Hkv, npre + T, d), 52, torch.bfloat16)
+    v = gen((Hkv, npre + T, d), 53, torch.bfloat16)
+    o1, l1 = tsw.tree_attn_verify(q, k, v, parent, npre)
+    mask, _ = tsw.tree_mask(parent)
+    # node 39 (a leaf) sees only its own ancestors; poison every other tree row
+    k2 = k.clone()
+    anc = [j for j in range(T) if (int(mask[39]) >> j) & 1]
+    others = [j for j in range(T) if j not in anc]
+    k2[:, [npre + j for j in others], :] = 1e4
+    o2, l2 = tsw.tree_attn_verify(q, k2, v, parent, npre)
+    torch.cuda.synchronize()
+    assert torch.equal(o1[39], o2[39]) and torch.equal(l1[39], l2[39])
+    assert torch.equal(o1[0], o2[0]) and torch.equal(l1[0], l2[0])
+    # nodes that do see poisoned rows change; all rows must match the oracle
+    o_ref, l_ref = oracle.tree_attn(wl.oracle_view(q), wl.oracle_view(k2), wl.oracle_view(v),
+                                    parent, npre, 1 / np.sqrt(d), nthreads=NTHREADS)
+    check(o2, l2, o_ref, l_ref, TOL["bf16"], "poisoned tree rows")
+
+
+@pytest.mark.parametrize("n_splits", [1, 2, 3, 7, 64, 300])
+def test_split_then_merge(n_splits):
+    """The two-phase API with caller-chosen split counts (including splits
+    with no keys) merges to the oracle result."""
+    T, Hq, Hkv, d, npre = 40, 32, 8, 128, 5000
+    parent = wl.kary_tree_parent(T, 3)
+    q = gen((T, Hq, d), 61, torch.bfloat16)
+    k = gen((Hkv, npre + T, d), 62, torch.bfloat16)
+    v = gen((Hkv, npre + T, d), 63, torch.bfloat16)
+    po, pl = tsw.tree_attn_split(q, k, v, parent, npre, n_splits)
+    o, lse = tsw.lse_merge(po, pl)
+    torch.cuda.synchronize()
+    o_ref, l_ref = oracle.tree_attn(wl.oracle_view(q), wl.oracle_view(k), wl.oracle_view(v),
+                                    parent, npre, 1 / np.sqrt(d), nthreads=NTHREADS)
+    check(o, lse, o_ref, l_ref, TOL["bf16"], "split %d" % n_splits)
+
+
+def test_lse_merge_against_oracle():
+    rng = np.random.default_rng(5)
+    S, R, d = 9, 300, 128
+    po = rng.standard_normal((S, R, d)).astype(np.float32)
+    pl = (rng.standard_normal((S, R)) * 5).astype(np.float32)
+    pl[2] = -np.inf
+    pl[5, :100] = -np.inf
+    o, lse = tsw.lse_merge(torch.from_numpy(po).cuda(), torch.from_numpy(pl).cuda())
+    torch.cuda.synchronize()
+    o_ref, l_ref = oracle.lse_merge(po.astype(np.float64), pl.astype(np.float64))
+    check(o, lse, o_ref, l_ref, 1e-5, "merge")
+
+
+def test_deterministic():
+    w = wl.WORKLOADS["gqa8b_8k"]
+    q, k, v = wl.make_qkv(w, device="cuda")
+    o0, l0 = tsw.tree_attn_verify(q, k, v, w.parent(), w.n_prefix)
+    for _ in range(5):
+        o1, l1 = tsw.tree_attn_verify(q, k, v, w.parent(), w.n_prefix)
+        assert torch.equal(o0, o1) and torch.equal(l0, l1)
+
+
+def test_small_workspace_rejected():
+    w = wl.WORKLOADS["gqa8b_8k"]
+    q, k, v = wl.make_qkv(w, device="cuda")
+    need = tsw.workspace_size(q, k, w.n_prefix)
+    ws = torch.empty(need - 256, dtype=torch.uint8, device=q.device)
+    with pytest.raises(tsw.TswError) as e:
+        tsw.tree_attn_verify(q, k, v, w.parent(), w.n_prefix, workspace=ws)
+    assert e.value.status == -5
+
+
+def test_planner_fills_the_chip():
+    import ctypes
+    w = wl.WORKLOADS["gqa8b_100k"]
+    desc = tsw.AttnDesc(T=w.n_nodes, Hq=w.Hq, Hkv=w.Hkv, d=w.d, n_prefix=w.n_prefix,
+                        kv_head_stride=w.cap * w.d, dtype=tsw.DTYPE_BF16, impl=0,
+                        scale=w.scale(), reserved=0)
+    n = ctypes.c_int32(0)
+    assert tsw.lib().tsw_plan_splits(ctypes.byref(desc), -1, ctypes.byref(n)) == 0
+    s = n.value
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    say("CUs %d splits %d" % (cus, s))
+    assert s * w.Hkv <= cus and s * w.Hkv > cus // 2

@@ -1,0 +1,299 @@
+"""ctypes binding of libtsw.so (include/tsw.h): argument marshalling only.
+
+Torch tensors supply device memory and the current HIP stream; every step of
+the computation runs in the library's kernels.  There is no fallback: if
+libtsw.so is missing or fails to load, every call raises.
+"""
+import ctypes
+import os
+import re
+
+import numpy as np
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libtsw.so")
+HEADER = os.path.join(os.path.dirname(_PKG), "include", "tsw.h")
+
+TSW_OK = 0
+DTYPE_F32, DTYPE_BF16 = 0, 1
+IMPL = {"auto": 0, "valu": 1, "mfma": 2}
+
+
+class TswError(RuntimeError):
+    def __init__(self, status, what):
+        super().__init__("%s: %s (status %d)" % (what, status_str(status), status))
+        self.status = status
+
+
+class AttnDesc(ctypes.Structure):
+    _fields_ = [
+        ("T", ctypes.c_int32), ("Hq", ctypes.c_int32), ("Hkv", ctypes.c_int32),
+        ("d", ctypes.c_int32), ("n_prefix", ctypes.c_int64), ("kv_head_stride", ctypes.c_int64),
+        ("dtype", ctypes.c_int32), ("impl", ctypes.c_int32), ("scale", ctypes.c_float),
+        ("reserved", ctypes.c_int32),
+    ]
+
+
+_lib = None
+
+
+def lib():
+    """The loaded library; raises if it was never built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError("libtsw.so is not built (run __graft_entry__.build() or "
+                           "python -m tree_verification_attention_tsw_amd.build); "
+                           "there is no CPU fallback")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    D = ctypes.POINTER(AttnDesc)
+    L.tsw_tree_mask_build.argtypes = [vp, i32, vp, vp]
+    L.tsw_plan_splits.argtypes = [D, i64, ctypes.POINTER(i32)]
+    L.tsw_workspace_size.argtypes = [D, i64, ctypes.POINTER(sz)]
+    L.tsw_tree_attn_verify.argtypes = [D, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.tsw_tree_attn_partial.argtypes = [D, vp, vp, vp, vp, vp, i64, vp, vp, vp, sz, vp]
+    L.tsw_tree_attn_split.argtypes = [D, vp, vp, vp, vp, vp, i64, i32, vp, vp, vp]
+    L.tsw_lse_merge.argtypes = [i32, i64, i32, vp, vp, vp, vp, vp]
+    L.tsw_status_str.argtypes = [ctypes.c_int]
+    L.tsw_status_str.restype = ctypes.c_char_p
+    for name in ("tsw_tree_mask_build", "tsw_plan_splits", "tsw_workspace_size",
+                 "tsw_tree_attn_verify", "tsw_tree_attn_partial", "tsw_tree_attn_split",
+                 "tsw_lse_merge"):
+        getattr(L, name).restype = ctypes.c_int
+    _lib = L
+    return L
+
+
+def declared_functions():
+    """Names of the functions include/tsw.h declares."""
+    with open(HEADER) as f:
+        text = f.read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(tsw_\w+)\s*\(", text, re.M)))
+
+
+def status_str(status):
+    return lib().tsw_status_str(int(status)).decode()
+
+
+def _check(rc, what):
+    if rc != TSW_OK:
+        raise TswError(rc, what)
+
+
+def _np_ptr(a):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _dev_ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+
+
+def _stream(t):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def tree_mask(parent):
+    """Host tree mask: (mask uint64[T], depth int32[T])."""
+    parent = np.ascontiguousarray(parent, dtype=np.int32)
+    T = parent.shape[0]
+    mask = np.zeros(max(T, 1), dtype=np.uint64)
+    depth = np.zeros(max(T, 1), dtype=np.int32)
+    _check(lib().tsw_tree_mask_build(_np_ptr(parent), T, _np_ptr(mask), _np_ptr(depth)),
+           "tsw_tree_mask_build")
+    return mask[:T], depth[:T]
+
+
+def make_desc(q, k, n_prefix, scale=None, impl="auto"):
+    """Descriptor for q [T, Hq, d] and a cache k [Hkv, rows, d]."""
+    T, Hq, d = q.shape
+    Hkv = k.shape[0]
+    if q.dtype == torch.float32:
+        dt = DTYPE_F32
+    elif q.dtype == torch.bfloat16:
+        dt = DTYPE_BF16
+    else:
+        raise TypeError("q/k/v must be float32 or bfloat16, got %s" % q.dtype)
+    desc = AttnDesc()
+    desc.T, desc.Hq, desc.Hkv, desc.d = T, Hq, Hkv, d
+    desc.n_prefix = int(n_prefix)
+    desc.kv_head_stride = int(k.stride(0))
+    desc.dtype = dt
+    desc.impl = IMPL[impl]
+    desc.scale = float(scale) if scale is not None else 1.0 / float(np.sqrt(d))
+    desc.reserved = 0
+    return desc
+
+
+def _check_tensors(q, k, v):
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not t.is_cuda:
+            raise ValueError("%s must be a GPU tensor" % name)
+    if not q.is_contiguous():
+        raise ValueError("q must be contiguous [T, Hq, d]")
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("q, k, v dtypes differ")
+    if k.shape != v.shape or k.stride() != v.stride():
+        raise ValueError("k and v must have the same shape and strides")
+    if k.dim() != 3 or k.stride(2) != 1 or k.stride(1) != k.shape[2] or k.shape[2] != q.shape[2]:
+        raise ValueError("k/v must be [Hkv, rows, d] with contiguous rows")
+
+
+def _parent_arr(parent):
+    return np.ascontiguousarray(parent, dtype=np.int32)
+
+
+def plan_splits(q, k, n_prefix, n_idx=-1, scale=None, impl="auto"):
+    desc = make_desc(q, k, n_prefix, scale, impl)
+    n = ctypes.c_int32(0)
+    _check(lib().tsw_plan_splits(ctypes.byref(desc), int(n_idx), ctypes.byref(n)), "tsw_plan_splits")
+    return n.value
+
+
+def workspace_size(q, k, n_prefix, n_idx=-1, scale=None, impl="auto"):
+    desc = make_desc(q, k, n_prefix, scale, impl)
+    n = ctypes.c_size_t(0)
+    _check(lib().tsw_workspace_size(ctypes.byref(desc), int(n_idx), ctypes.byref(n)),
+           "tsw_workspace_size")
+    return n.value
+
+
+def _workspace(q, k, n_prefix, n_idx, scale, impl, workspace):
+    need = workspace_size(q, k, n_prefix, n_idx, scale, impl)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    return workspace
+
+
+def tree_attn_verify(q, k, v, parent, n_prefix, scale=None, impl="auto", out=None, workspace=None):
+    """Tree verification attention; returns (o [T, Hq, d] float32, lse [T, Hq] float32)."""
+    _check_tensors(q, k, v)
+    T, Hq, d = q.shape
+    desc = make_desc(q, k, n_prefix, scale, impl)
+    o, lse = out if out is not None else (
+        torch.empty((T, Hq, d), dtype=torch.float32, device=q.device),
+        torch.empty((T, Hq), dtype=torch.float32, device=q.device))
+    ws = _workspace(q, k, n_prefix, -1, scale, impl, workspace)
+    p = _parent_arr(parent)
+    _check(lib().tsw_tree_attn_verify(ctypes.byref(desc), _dev_ptr(q), _dev_ptr(k), _dev_ptr(v),
+                                      _np_ptr(p), _dev_ptr(o), _dev_ptr(lse), _dev_ptr(ws),
+                                      ws.numel(), _stream(q)), "tsw_tree_attn_verify")
+    return o, lse
+
+
+def tree_attn_partial(q, k, v, parent, idx, n_prefix, scale=None, impl="auto", out=None,
+                      workspace=None):
+    """Partial-KV (draft pass) attention over idx (int32 device tensor)."""
+    _check_tensors(q, k, v)
+    if idx.dtype != torch.int32 or not idx.is_cuda or not idx.is_contiguous():
+        raise ValueError("idx must be a contiguous int32 GPU tensor")
+    T, Hq, d = q.shape
+    n_idx = idx.numel()
+    desc = make_desc(q, k, n_prefix, scale, impl)
+    o, lse = out if out is not None else (
+        torch.empty((T, Hq, d), dtype=torch.float32, device=q.device),
+        torch.empty((T, Hq), dtype=torch.float32, device=q.device))
+    ws = _workspace(q, k, n_prefix, n_idx, scale, impl, workspace)
+    p = _parent_arr(parent)
+    _check(lib().tsw_tree_attn_partial(ctypes.byref(desc), _dev_ptr(q), _dev_ptr(k), _dev_ptr(v),
+                                       _np_ptr(p), _dev_ptr(idx) if n_idx else None, n_idx,
+                                       _dev_ptr(o), _dev_ptr(lse), _dev_ptr(ws), ws.numel(),
+                                       _stream(q)), "tsw_tree_attn_partial")
+    return o, lse
+
+
+def tree_attn_split(q, k, v, parent, n_prefix, n_splits, idx=None, scale=None, impl="auto",
+                    out=None):
+    """First phase only: per-split (part_o [S, T, Hq, d], part_lse [S, T, Hq])."""
+    _check_tensors(q, k, v)
+    T, Hq, d = q.shape
+    desc = make_desc(q, k, n_prefix, scale, impl)
+    po, pl = out if out is not None else (
+        torch.empty((n_splits, T, Hq, d), dtype=torch.float32, device=q.device),
+        torch.empty((n_splits, T, Hq), dtype=torch.float32, device=q.device))
+    p = _parent_arr(parent)
+    n_idx = idx.numel() if idx is not None else 0
+    idx_ptr = _dev_ptr(idx) if idx is not None else None
+    if idx is not None and n_idx == 0:
+        idx_ptr = _dev_ptr(po)  # non-null marker for the partial variant; never read
+    _check(lib().tsw_tree_attn_split(ctypes.byref(desc), _dev_ptr(q), _dev_ptr(k), _dev_ptr(v),
+                                     _np_ptr(p), idx_ptr, n_idx, int(n_splits), _dev_ptr(po),
+                                     _dev_ptr(pl), _stream(q)), "tsw_tree_attn_split")
+    return po, pl
+
+
+def lse_merge(part_o, part_lse, out=None):
+    """Merge partial results: part_o [S, ..., d], part_lse [S, ...] -> (o, lse)."""
+    S = part_o.shape[0]
+    d = part_o.shape[-1]
+    rows = part_lse[0].numel()
+    if not (part_o.is_contiguous() and part_lse.is_contiguous()):
+        raise ValueError("partials must be contiguous")
+    if part_o.dtype != torch.float32 or part_lse.dtype != torch.float32:
+        raise TypeError("partials must be float32")
+    o, lse = out if out is not None else (
+        torch.empty(part_o.shape[1:], dtype=torch.float32, device=part_o.device),
+        torch.empty(part_lse.shape[1:], dtype=torch.float32, device=part_o.device))
+    _check(lib().tsw_lse_merge(S, rows, d, _dev_ptr(part_o), _dev_ptr(part_lse), _dev_ptr(o),
+                               _dev_ptr(lse), _stream(part_o)), "tsw_lse_merge")
+    return o, lse
+
+
+class PreparedCall:
+    """A C entry point with every argument marshalled once, for tight loops
+    (benchmarks, serving): calling it costs one ctypes call."""
+
+    def __init__(self, fn, args, what, keep):
+        self._fn, self._args, self._what, self._keep = fn, args, what, keep
+
+    def __call__(self):
+        rc = self._fn(*self._args)
+        if rc != TSW_OK:
+            raise TswError(rc, self._what)
+
+
+def prepare_verify(q, k, v, parent, n_prefix, o, lse, workspace, idx=None, scale=None,
+                   impl="auto", stream=None):
+    """Bound tsw_tree_attn_verify (idx None) or tsw_tree_attn_partial call."""
+    _check_tensors(q, k, v)
+    desc = make_desc(q, k, n_prefix, scale, impl)
+    p = _parent_arr(parent)
+    st = ctypes.c_void_p(stream.cuda_stream if stream is not None
+                         else torch.cuda.current_stream(q.device).cuda_stream)
+    L = lib()
+    if idx is None:
+        args = (ctypes.byref(desc), _dev_ptr(q), _dev_ptr(k), _dev_ptr(v), _np_ptr(p), _dev_ptr(o),
+                _dev_ptr(lse), _dev_ptr(workspace), workspace.numel(), st)
+        return PreparedCall(L.tsw_tree_attn_verify, args, "tsw_tree_attn_verify", (desc, p))
+    args = (ctypes.byref(desc), _dev_ptr(q), _dev_ptr(k), _dev_ptr(v), _np_ptr(p),
+            _dev_ptr(idx) if idx.numel() else None, idx.numel(), _dev_ptr(o), _dev_ptr(lse),
+            _dev_ptr(workspace), workspace.numel(), st)
+    return PreparedCall(L.tsw_tree_attn_partial, args, "tsw_tree_attn_partial", (desc, p))
+
+
+def prepare_split(q, k, v, parent, n_prefix, n_splits, part_o, part_lse, idx=None, scale=None,
+                  impl="auto", stream=None):
+    """Bound tsw_tree_attn_split call (first phase only)."""
+    _check_tensors(q, k, v)
+    desc = make_desc(q, k, n_prefix, scale, impl)
+    p = _parent_arr(parent)
+    st = ctypes.c_void_p(stream.cuda_stream if stream is not None
+                         else torch.cuda.current_stream(q.device).cuda_stream)
+    idx_ptr = _dev_ptr(idx) if idx is not None else None
+    if idx is not None and idx.numel() == 0:
+        idx_ptr = _dev_ptr(part_o)
+    args = (ctypes.byref(desc), _dev_ptr(q), _dev_ptr(k), _dev_ptr(v), _np_ptr(p), idx_ptr,
+            0 if idx is None else idx.numel(), int(n_splits), _dev_ptr(part_o), _dev_ptr(part_lse),
+            st)
+    return PreparedCall(lib().tsw_tree_attn_split, args, "tsw_tree_attn_split", (desc, p))
+
+
+def prepare_merge(part_o, part_lse, o, lse, stream=None):
+    """Bound tsw_lse_merge call (second phase only)."""
+    st = ctypes.c_void_p(stream.cuda_stream if stream is not None
+                         else torch.cuda.current_stream(part_o.device).cuda_stream)
+    args = (part_o.shape[0], part_lse[0].numel(), part_o.shape[-1], _dev_ptr(part_o),
+            _dev_ptr(part_lse), _dev_ptr(o), _dev_ptr(lse), st)
+    return PreparedCall(lib().tsw_lse_merge, args, "tsw_lse_merge", None)

@@ -1,0 +1,288 @@
+// Host side of the tree-verification attention library: argument checks,
+// the tree mask builder, the split planner and the C entry points declared
+// in include/tsw.h.  Kernels live in tsw_kernels.hip.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <atomic>
+
+#include "tsw.h"
+#include "tsw_internal.h"
+
+namespace {
+
+using tsw::SplitArgs;
+
+constexpr int kMaxNodes = 64;
+constexpr float kLog2e = 1.44269504088896340736f;
+
+// Parent encoding of the candidate tree: a single root at index 0
+// (parent -1), every other node names an earlier node.  A breadth-first
+// numbering of the 3-ary draft tree ("From Hours to Minutes ..." arxivlens
+// summary, Technical Contribution) satisfies this, as does any topological
+// order.
+int build_mask(const int32_t* parent, int32_t T, uint64_t* mask, int32_t* depth) {
+    if (!parent || !mask) return TSW_EINVAL;
+    if (T < 1 || T > kMaxNodes) return TSW_EINVAL;
+    if (parent[0] != -1) return TSW_EBADTREE;
+    for (int32_t i = 1; i < T; ++i)
+        if (parent[i] < 0 || parent[i] >= i) return TSW_EBADTREE;
+    // Parents precede children, so one forward pass extends each parent's
+    // ancestor-or-self set by the node itself.
+    mask[0] = 1ull;
+    if (depth) depth[0] = 0;
+    for (int32_t i = 1; i < T; ++i) {
+        mask[i] = mask[parent[i]] | (1ull << i);
+        if (depth) depth[i] = depth[parent[i]] + 1;
+    }
+    return TSW_OK;
+}
+
+int check_desc(const tsw_attn_desc* d) {
+    if (!d) return TSW_EINVAL;
+    if (d->reserved != 0) return TSW_EINVAL;
+    if (d->T < 1 || d->T > kMaxNodes) return TSW_EINVAL;
+    if (d->Hq < 1 || d->Hkv < 1 || d->Hq % d->Hkv != 0) return TSW_EINVAL;
+    if (d->n_prefix < 0) return TSW_EINVAL;
+    if (!(d->scale > 0.0f) || !isfinite(d->scale)) return TSW_EINVAL;
+    if (d->d != 64 && d->d != 128) return TSW_EUNSUPPORTED;
+    if (d->dtype != TSW_DTYPE_F32 && d->dtype != TSW_DTYPE_BF16) return TSW_EUNSUPPORTED;
+    if (d->impl != TSW_IMPL_AUTO && d->impl != TSW_IMPL_VALU && d->impl != TSW_IMPL_MFMA) return TSW_EUNSUPPORTED;
+    if (d->kv_head_stride < (d->n_prefix + d->T) * (int64_t)d->d) return TSW_EINVAL;
+    // Rows per kv head (T * G) bound the kernels' register tiles.
+    const int64_t M = (int64_t)d->T * (d->Hq / d->Hkv);
+    if (M > 4096) return TSW_EUNSUPPORTED;
+    if (d->impl == TSW_IMPL_MFMA) {
+        tsw::MfmaConfig cfg;
+        if (d->dtype != TSW_DTYPE_BF16 || d->d != 128 || !tsw::mfma_config_for((int)M, &cfg))
+            return TSW_EUNSUPPORTED;
+    }
+    return TSW_OK;
+}
+
+bool use_mfma(const tsw_attn_desc* d, tsw::MfmaConfig* cfg) {
+    if (d->impl == TSW_IMPL_VALU) return false;
+    if (d->dtype != TSW_DTYPE_BF16 || d->d != 128) return false;
+    return tsw::mfma_config_for(d->T * (d->Hq / d->Hkv), cfg);
+}
+
+// Compute units of the current device, cached per device ordinal.
+int device_cus(int* cus) {
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return TSW_EHIP;
+    if (dev >= 0 && dev < 64) {
+        const int c = cache[dev].load(std::memory_order_relaxed);
+        if (c > 0) {
+            *cus = c;
+            return TSW_OK;
+        }
+    }
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+        return TSW_EHIP;
+    if (dev >= 0 && dev < 64) cache[dev].store(n, std::memory_order_relaxed);
+    *cus = n;
+    return TSW_OK;
+}
+
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Split-K degree: enough work-groups to occupy every CU once (the matrix
+// kernel runs one work-group per CU), no split shorter than two key tiles,
+// and gather slices that fit the LDS index buffer.
+int plan(const tsw_attn_desc* d, int64_t n_keys, bool gather, int cus, int32_t* n_splits) {
+    tsw::MfmaConfig cfg;
+    int64_t s;
+    if (use_mfma(d, &cfg)) {
+        const int64_t tk = cfg.tile_keys();
+        s = cus / d->Hkv;
+        if (s < 1) s = 1;
+        const int64_t by_len = cdiv(n_keys, 2 * tk);
+        if (s > by_len) s = by_len;
+    } else {
+        const int64_t nrb = cdiv((int64_t)d->T * (d->Hq / d->Hkv), tsw::kValuRows);
+        s = (2 * (int64_t)cus) / (d->Hkv * nrb);
+        if (s < 1) s = 1;
+        const int64_t by_len = cdiv(n_keys, 2 * tsw::kValuTile);
+        if (s > by_len) s = by_len;
+    }
+    if (gather) {
+        const int64_t need = cdiv(n_keys, tsw::kGatherChunkMax);
+        if (s < need) s = need;
+    }
+    if (s < 1) s = 1;
+    if (s > 65535) return TSW_EUNSUPPORTED;
+    *n_splits = (int32_t)s;
+    return TSW_OK;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+size_t ws_bytes_for(const tsw_attn_desc* d, int32_t n_splits) {
+    const size_t rows = (size_t)d->T * d->Hq;
+    return align256((size_t)n_splits * rows * d->d * sizeof(float)) +
+           align256((size_t)n_splits * rows * sizeof(float));
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? TSW_OK : TSW_EHIP; }
+
+int run_split(const tsw_attn_desc* d, const void* q, const void* k, const void* v,
+              const int32_t* parent, const int32_t* idx, int64_t n_idx, int32_t n_splits,
+              float* part_o, float* part_lse, hipStream_t stream) {
+    const bool gather = idx != nullptr;
+    const int64_t n_keys = gather ? n_idx : d->n_prefix;
+    SplitArgs a;
+    memset(&a, 0, sizeof a);
+    int rc = build_mask(parent, d->T, a.mask, nullptr);
+    if (rc != TSW_OK) return rc;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.idx = idx;
+    a.part_o = part_o;
+    a.part_lse = part_lse;
+    a.n_prefix = d->n_prefix;
+    a.kv_head_stride = d->kv_head_stride;
+    a.n_keys = n_keys;
+    a.T = d->T;
+    a.Hq = d->Hq;
+    a.Hkv = d->Hkv;
+    a.G = d->Hq / d->Hkv;
+    a.M = a.T * a.G;
+    a.n_splits = n_splits;
+    a.scale_log2 = d->scale * kLog2e;
+
+    tsw::MfmaConfig cfg;
+    if (use_mfma(d, &cfg)) {
+        const int64_t tk = cfg.tile_keys();
+        a.chunk_keys = cdiv(cdiv(n_keys, n_splits), tk) * tk;
+        if (gather && a.chunk_keys > tsw::kGatherChunkMax) return TSW_EUNSUPPORTED;
+        if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v) & 15) return TSW_EINVAL;
+        if (d->kv_head_stride % 8) return TSW_EINVAL;
+        return hip_status(tsw::launch_split_mfma(cfg, gather, a, d->Hkv, stream));
+    }
+    a.chunk_keys = cdiv(cdiv(n_keys, n_splits), tsw::kValuTile) * tsw::kValuTile;
+    return hip_status(tsw::launch_split_valu(d->dtype, d->d, gather, a, d->Hkv, stream));
+}
+
+int check_common(const tsw_attn_desc* d, const void* q, const void* k, const void* v,
+                 const int32_t* parent, const void* o, const void* lse) {
+    int rc = check_desc(d);
+    if (rc != TSW_OK) return rc;
+    if (!q || !k || !v || !parent || !o || !lse) return TSW_EINVAL;
+    uint64_t mask[kMaxNodes];
+    return build_mask(parent, d->T, mask, nullptr);
+}
+
+int full_call(const tsw_attn_desc* d, const void* q, const void* k, const void* v,
+              const int32_t* parent, const int32_t* idx, int64_t n_idx, float* o, float* lse,
+              void* ws, size_t ws_bytes, tsw_stream_t stream) {
+    int rc = check_common(d, q, k, v, parent, o, lse);
+    if (rc != TSW_OK) return rc;
+    const bool gather = n_idx >= 0;
+    if (gather && (n_idx > d->n_prefix)) return TSW_EBADINDEX;
+    if (gather && n_idx > 0 && !idx) return TSW_EINVAL;
+    if (!ws) return TSW_EINVAL;
+    if ((uintptr_t)ws & 255) return TSW_EINVAL;
+    int cus = 0;
+    rc = device_cus(&cus);
+    if (rc != TSW_OK) return rc;
+    int32_t n_splits = 0;
+    rc = plan(d, gather ? n_idx : d->n_prefix, gather, cus, &n_splits);
+    if (rc != TSW_OK) return rc;
+    if (ws_bytes < ws_bytes_for(d, n_splits)) return TSW_ENOSPACE;
+    const size_t rows = (size_t)d->T * d->Hq;
+    float* part_o = (float*)ws;
+    float* part_lse = (float*)((char*)ws + align256((size_t)n_splits * rows * d->d * sizeof(float)));
+    // An empty index list still needs a non-null pointer for the gather
+    // kernel's "partial" mode; no entry of it is read.
+    const int32_t* idx_arg = gather ? (idx ? idx : (const int32_t*)ws) : nullptr;
+    rc = run_split(d, q, k, v, parent, idx_arg, gather ? n_idx : 0, n_splits, part_o, part_lse,
+                   (hipStream_t)stream);
+    if (rc != TSW_OK) return rc;
+    return hip_status(tsw::launch_lse_merge(n_splits, (int64_t)rows, d->d, part_o, part_lse, o, lse,
+                                            (hipStream_t)stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+int tsw_tree_mask_build(const int32_t* parent, int32_t T, uint64_t* mask, int32_t* depth) {
+    return build_mask(parent, T, mask, depth);
+}
+
+int tsw_plan_splits(const tsw_attn_desc* desc, int64_t n_idx, int32_t* n_splits) {
+    int rc = check_desc(desc);
+    if (rc != TSW_OK) return rc;
+    if (!n_splits) return TSW_EINVAL;
+    if (n_idx > desc->n_prefix) return TSW_EBADINDEX;
+    int cus = 0;
+    rc = device_cus(&cus);
+    if (rc != TSW_OK) return rc;
+    const bool gather = n_idx >= 0;
+    return plan(desc, gather ? n_idx : desc->n_prefix, gather, cus, n_splits);
+}
+
+int tsw_workspace_size(const tsw_attn_desc* desc, int64_t n_idx, size_t* bytes) {
+    if (!bytes) return TSW_EINVAL;
+    int32_t s = 0;
+    int rc = tsw_plan_splits(desc, n_idx, &s);
+    if (rc != TSW_OK) return rc;
+    *bytes = ws_bytes_for(desc, s);
+    return TSW_OK;
+}
+
+int tsw_tree_attn_verify(const tsw_attn_desc* desc, const void* q, const void* k, const void* v,
+                         const int32_t* parent, float* o, float* lse, void* workspace,
+                         size_t workspace_bytes, tsw_stream_t stream) {
+    return full_call(desc, q, k, v, parent, nullptr, -1, o, lse, workspace, workspace_bytes, stream);
+}
+
+int tsw_tree_attn_partial(const tsw_attn_desc* desc, const void* q, const void* k, const void* v,
+                          const int32_t* parent, const int32_t* idx, int64_t n_idx, float* o,
+                          float* lse, void* workspace, size_t workspace_bytes,
+                          tsw_stream_t stream) {
+    if (n_idx < 0) return TSW_EBADINDEX;
+    return full_call(desc, q, k, v, parent, idx, n_idx, o, lse, workspace, workspace_bytes, stream);
+}
+
+int tsw_tree_attn_split(const tsw_attn_desc* desc, const void* q, const void* k, const void* v,
+                        const int32_t* parent, const int32_t* idx, int64_t n_idx,
+                        int32_t n_splits, float* part_o, float* part_lse, tsw_stream_t stream) {
+    int rc = check_common(desc, q, k, v, parent, part_o, part_lse);
+    if (rc != TSW_OK) return rc;
+    if (n_splits < 1 || n_splits > 65535) return TSW_EINVAL;
+    if (idx) {
+        if (n_idx < 0 || n_idx > desc->n_prefix) return TSW_EBADINDEX;
+    }
+    return run_split(desc, q, k, v, parent, idx, idx ? n_idx : 0, n_splits, part_o, part_lse,
+                     (hipStream_t)stream);
+}
+
+int tsw_lse_merge(int32_t n_splits, int64_t n_rows, int32_t d, const float* part_o,
+                  const float* part_lse, float* o, float* lse, tsw_stream_t stream) {
+    if (n_splits < 1 || n_rows < 0 || d < 1) return TSW_EINVAL;
+    if (n_rows > 0 && (!part_o || !part_lse || !o || !lse)) return TSW_EINVAL;
+    return hip_status(tsw::launch_lse_merge(n_splits, n_rows, d, part_o, part_lse, o, lse,
+                                            (hipStream_t)stream));
+}
+
+const char* tsw_status_str(int status) {
+    switch (status) {
+        case TSW_OK: return "ok";
+        case TSW_EINVAL: return "invalid argument";
+        case TSW_EBADTREE: return "parent[] is not a tree rooted at node 0 with parents before children";
+        case TSW_EBADINDEX: return "index list size out of range";
+        case TSW_EUNSUPPORTED: return "unsupported head dim, dtype, shape or implementation";
+        case TSW_ENOSPACE: return "workspace too small";
+        case TSW_EHIP: return "HIP runtime error";
+        default: return "unknown status";
+    }
+}
+
+}  // extern "C"

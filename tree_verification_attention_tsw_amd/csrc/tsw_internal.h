@@ -1,0 +1,56 @@
+// Internal interface between the host API (tsw_api.cpp) and the gfx950
+// kernels (tsw_kernels.hip).  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tsw {
+
+// Everything a split kernel needs, passed by value as the kernel argument.
+// The tree mask travels here (one 64-bit word per node) so that no device
+// buffer or host-to-device copy is needed for it.
+struct SplitArgs {
+    const void* q;           // [T][Hq][d]
+    const void* k;           // [Hkv][rows][d], kv_head_stride elements per head
+    const void* v;
+    const int32_t* idx;      // partial variant: sorted prefix positions; nullptr for verify
+    float* part_o;           // [n_splits][T][Hq][d]
+    float* part_lse;         // [n_splits][T][Hq], natural log
+    int64_t n_prefix;        // the tree rows start at this cache position
+    int64_t kv_head_stride;  // elements
+    int64_t n_keys;          // prefix keys in the list: n_prefix (verify) or n_idx (partial)
+    int64_t chunk_keys;      // prefix keys per split, a multiple of the kernel's key tile
+    int32_t T, Hq, Hkv, G, M, n_splits;
+    float scale_log2;        // scale * log2(e): scores are exponentiated base 2
+    int32_t pad_;
+    uint64_t mask[64];       // ancestor-or-self bits per node
+};
+
+// Matrix-core kernel shapes.  A work-group holds `waves` wavefronts: `rgroups`
+// groups of query-row blocks (16 rows each, at most `nb` blocks per wave)
+// times waves/rgroups sub-tiles of 32 keys per key tile.
+struct MfmaConfig {
+    int waves, rgroups, nb;
+    int tile_keys() const { return 32 * (waves / rgroups); }
+};
+
+// Largest index-list slice one work-group stages in LDS (gather variant).
+constexpr int kGatherChunkMax = 4096;
+
+// Picks the matrix-core shape for M query rows per kv head; returns false
+// when no shape covers M (callers then use the vector-ALU kernel).
+bool mfma_config_for(int M, MfmaConfig* cfg);
+
+hipError_t launch_split_mfma(const MfmaConfig& cfg, bool gather, const SplitArgs& a,
+                             int n_kv_heads, hipStream_t stream);
+hipError_t launch_split_valu(int dtype, int d, bool gather, const SplitArgs& a, int n_kv_heads,
+                             hipStream_t stream);
+hipError_t launch_lse_merge(int n_splits, int64_t n_rows, int d, const float* part_o,
+                            const float* part_lse, float* o, float* lse, hipStream_t stream);
+
+// Key tile of the vector-ALU kernel and its query rows per work-group.
+constexpr int kValuTile = 64;
+constexpr int kValuRows = 16;
+
+}  // namespace tsw
