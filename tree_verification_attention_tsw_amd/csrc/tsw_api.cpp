@@ -63,9 +63,16 @@ int check_desc(const tsw_attn_desc* d) {
     return TSW_OK;
 }
 
-bool use_mfma(const tsw_attn_desc* d, tsw::MfmaConfig* cfg) {
+// Prefix lists shorter than this go to the vector-ALU kernel under
+// TSW_IMPL_AUTO: the work is a few tiles, and its fp32 softmax weights avoid
+// the bf16 rounding of P that the matrix path applies, which matters most
+// when only a handful of keys carry the weight.
+constexpr int64_t kMfmaMinKeys = 256;
+
+bool use_mfma(const tsw_attn_desc* d, int64_t n_keys, tsw::MfmaConfig* cfg) {
     if (d->impl == TSW_IMPL_VALU) return false;
     if (d->dtype != TSW_DTYPE_BF16 || d->d != 128) return false;
+    if (d->impl == TSW_IMPL_AUTO && n_keys < kMfmaMinKeys) return false;
     return tsw::mfma_config_for(d->T * (d->Hq / d->Hkv), cfg);
 }
 
@@ -97,7 +104,7 @@ int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 int plan(const tsw_attn_desc* d, int64_t n_keys, bool gather, int cus, int32_t* n_splits) {
     tsw::MfmaConfig cfg;
     int64_t s;
-    if (use_mfma(d, &cfg)) {
+    if (use_mfma(d, n_keys, &cfg)) {
         const int64_t tk = cfg.tile_keys();
         s = cus / d->Hkv;
         if (s < 1) s = 1;
@@ -157,7 +164,7 @@ int run_split(const tsw_attn_desc* d, const void* q, const void* k, const void* 
     a.scale_log2 = d->scale * kLog2e;
 
     tsw::MfmaConfig cfg;
-    if (use_mfma(d, &cfg)) {
+    if (use_mfma(d, n_keys, &cfg)) {
         const int64_t tk = cfg.tile_keys();
         a.chunk_keys = cdiv(cdiv(n_keys, n_splits), tk) * tk;
         if (gather && a.chunk_keys > tsw::kGatherChunkMax) return TSW_EUNSUPPORTED;

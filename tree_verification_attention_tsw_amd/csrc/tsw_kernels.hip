@@ -37,6 +37,7 @@ namespace tsw {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 
@@ -104,7 +105,8 @@ __global__ __launch_bounds__(WAVES * 64, 1) void split_mfma(const SplitArgs a) {
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int w = tid >> 6;
+    // wave index as a scalar, so per-wave conditions compile to scalar branches
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int rg = w / KS;   // query-row group of this wave
     const int ks = w % KS;   // 32-key sub-tile of this wave
     const int li = lane & 15;
@@ -132,25 +134,27 @@ __global__ __launch_bounds__(WAVES * 64, 1) void split_mfma(const SplitArgs a) {
     }
 
     // Q^T as the B operand: lane (li, lj) holds query row li of the block,
-    // head-dim elements 32*s + 8*lj .. +7.
+    // head-dim elements 32*s + 8*lj .. +7.  Loads are unconditional (rows past
+    // M read row 0 and are zeroed) and drained before the K/V pipeline starts,
+    // so no wait for them is ever needed inside the tile loop.
     bf16x8 qop[NB][4];
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
         const int r = (rg + b * R) * 16 + li;
         const bool ok = b < nb_act && r < a.M;
         const int t = ok ? r / a.G : 0;
-        const int h = g * a.G + (ok ? r % a.G : 0);
+        const int h = ok ? g * a.G + r % a.G : 0;
         const bf16x8* src = (const bf16x8*)((const __bf16*)a.q + ((size_t)t * a.Hq + h) * 128 + 8 * lj);
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            if (ok) {
-                qop[b][s] = src[4 * s];
-            } else {
+        for (int s = 0; s < 4; ++s) qop[b][s] = src[4 * s];
+        if (!ok) {
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
 #pragma unroll
                 for (int e = 0; e < 8; ++e) qop[b][s][e] = (__bf16)0.0f;
-            }
         }
     }
+    wait_vmcnt<0>();
 
     // One tile = TK K rows then TK V rows; each DMA instruction moves four
     // 256-byte rows (64 lanes x 16 bytes) into consecutive LDS.  Rows past the
@@ -282,14 +286,20 @@ __global__ __launch_bounds__(WAVES * 64, 1) void split_mfma(const SplitArgs a) {
                 m_run[b] = mnew;
             }
             const float mu = m_run[b] == -INFINITY ? 0.0f : m_run[b];
+            // p is rounded to bf16 for the PV product; the row sum adds the
+            // same rounded values (v_dot2c_f32_bf16 with (1, 1)), so the
+            // normalisation matches the weights actually applied to V.
+            const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
             float lsum = 0.0f;
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const float p = exp2_fast(fmaf(sc[kb][b][i], c, -mu));
-                    lsum += p;
-                    pb[b][kb * 4 + i] = (__bf16)p;
+                for (int i = 0; i < 4; i += 2) {
+                    const bf16x2 pp = {(__bf16)exp2_fast(fmaf(sc[kb][b][i], c, -mu)),
+                                       (__bf16)exp2_fast(fmaf(sc[kb][b][i + 1], c, -mu))};
+                    lsum = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, lsum, false);
+                    pb[b][kb * 4 + i] = pp[0];
+                    pb[b][kb * 4 + i + 1] = pp[1];
                 }
             l_run[b] += lsum;
         }
@@ -512,10 +522,73 @@ __global__ __launch_bounds__(256) void split_valu(const SplitArgs a) {
 // ---------------------------------------------------------------------------
 // Log-sum-exp merge of split results
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void lse_merge(int n_splits, int64_t n_rows, int d,
+// One wavefront per output row: lanes hold the split LSEs (64 at a time),
+// wave reductions give the row's LSE, and each lane accumulates d/64
+// consecutive columns over the splits with coalesced loads.
+template <int D>
+__global__ __launch_bounds__(256) void lse_merge(int n_splits, int64_t n_rows,
                                                  const float* __restrict__ part_o,
                                                  const float* __restrict__ part_lse,
                                                  float* __restrict__ o, float* __restrict__ lse) {
+    constexpr int PER = D / 64;
+    constexpr float kLog2e = 1.44269504088896340736f;
+    const int lane = threadIdx.x & 63;
+    const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (r >= n_rows) return;
+    float mx = -INFINITY;
+    for (int s0 = 0; s0 < n_splits; s0 += 64)
+        if (s0 + lane < n_splits) mx = fmaxf(mx, part_lse[(int64_t)(s0 + lane) * n_rows + r]);
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) mx = xor_max(mx, m);
+    float acc[PER];
+#pragma unroll
+    for (int e = 0; e < PER; ++e) acc[e] = 0.0f;
+    if (mx == -INFINITY) {
+#pragma unroll
+        for (int e = 0; e < PER; ++e) o[r * D + lane * PER + e] = 0.0f;
+        if (lane == 0) lse[r] = -INFINITY;
+        return;
+    }
+    float sum = 0.0f;
+    for (int s0 = 0; s0 < n_splits; s0 += 64)
+        if (s0 + lane < n_splits) {
+            const float ls = part_lse[(int64_t)(s0 + lane) * n_rows + r];
+            sum += ls == -INFINITY ? 0.0f : exp2f((ls - mx) * kLog2e);
+        }
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) sum = xor_sum(sum, m);
+    const float L = mx + logf(sum);
+    for (int s0 = 0; s0 < n_splits; s0 += 64) {
+        float wl = 0.0f;
+        if (s0 + lane < n_splits) {
+            const float ls = part_lse[(int64_t)(s0 + lane) * n_rows + r];
+            wl = ls == -INFINITY ? 0.0f : exp2f((ls - L) * kLog2e);
+        }
+        const int n = n_splits - s0 < 64 ? n_splits - s0 : 64;
+#pragma unroll 8
+        for (int j = 0; j < n; ++j) {
+            const float wj = __shfl(wl, j);
+            const float* src = part_o + ((int64_t)(s0 + j) * n_rows + r) * D + lane * PER;
+            if constexpr (PER == 2) {
+                const float2 x = *(const float2*)src;
+                acc[0] = fmaf(wj, x.x, acc[0]);
+                acc[1] = fmaf(wj, x.y, acc[1]);
+            } else {
+#pragma unroll
+                for (int e = 0; e < PER; ++e) acc[e] = fmaf(wj, src[e], acc[e]);
+            }
+        }
+    }
+#pragma unroll
+    for (int e = 0; e < PER; ++e) o[r * D + lane * PER + e] = acc[e];
+    if (lane == 0) lse[r] = L;
+}
+
+// Any head dim: one thread per output element (used for d other than 64/128).
+__global__ __launch_bounds__(256) void lse_merge_generic(int n_splits, int64_t n_rows, int d,
+                                                         const float* __restrict__ part_o,
+                                                         const float* __restrict__ part_lse,
+                                                         float* __restrict__ o, float* __restrict__ lse) {
     const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (e >= n_rows * d) return;
     const int64_t r = e / d;
@@ -529,7 +602,10 @@ __global__ __launch_bounds__(256) void lse_merge(int n_splits, int64_t n_rows, i
         return;
     }
     float sum = 0.0f;
-    for (int s = 0; s < n_splits; ++s) sum += exp2f((part_lse[s * n_rows + r] - mx) * kLog2e);
+    for (int s = 0; s < n_splits; ++s) {
+        const float ls = part_lse[s * n_rows + r];
+        if (ls != -INFINITY) sum += exp2f((ls - mx) * kLog2e);
+    }
     const float L = mx + logf(sum);
     float acc = 0.0f;
     for (int s = 0; s < n_splits; ++s) {
@@ -595,10 +671,18 @@ hipError_t launch_split_valu(int dtype, int d, bool gather, const SplitArgs& a, 
 
 hipError_t launch_lse_merge(int n_splits, int64_t n_rows, int d, const float* part_o,
                             const float* part_lse, float* o, float* lse, hipStream_t stream) {
+    if (n_rows == 0) return hipSuccess;
+    if (d == 128 || d == 64) {
+        const dim3 grid((unsigned)((n_rows + 3) / 4));
+        if (d == 128)
+            hipLaunchKernelGGL(lse_merge<128>, grid, dim3(256), 0, stream, n_splits, n_rows, part_o, part_lse, o, lse);
+        else
+            hipLaunchKernelGGL(lse_merge<64>, grid, dim3(256), 0, stream, n_splits, n_rows, part_o, part_lse, o, lse);
+        return hipGetLastError();
+    }
     const int64_t n = n_rows * d;
-    if (n == 0) return hipSuccess;
     const dim3 grid((unsigned)((n + 255) / 256));
-    hipLaunchKernelGGL(lse_merge, grid, dim3(256), 0, stream, n_splits, n_rows, d, part_o, part_lse, o, lse);
+    hipLaunchKernelGGL(lse_merge_generic, grid, dim3(256), 0, stream, n_splits, n_rows, d, part_o, part_lse, o, lse);
     return hipGetLastError();
 }
 
