@@ -341,3 +341,26 @@ def test_planner_fills_the_chip():
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     say("CUs %d splits %d" % (cus, s))
     assert s * w.Hkv <= cus and s * w.Hkv > cus // 2
+
+
+@pytest.mark.parametrize("where", ["first_tile", "late_tile", "tree_row"])
+def test_large_logit_headroom(where):
+    """A key whose score is ~60 nats above every other score.  When it is
+    not in a split's first tile, the fast pass flags its rows and the
+    work-group reruns the split with exact row maxima; either way the
+    result must match the oracle."""
+    T, Hq, Hkv, d, npre = 40, 32, 8, 128, 4096
+    parent = wl.kary_tree_parent(T, 3)
+    q = gen((T, Hq, d), 81, torch.bfloat16)
+    k = gen((Hkv, npre + T, d), 82, torch.bfloat16)
+    v = gen((Hkv, npre + T, d), 83, torch.bfloat16)
+    pos = {"first_tile": 0, "late_tile": 3000, "tree_row": npre + 7}[where]
+    # K row aligned with the mean query direction of head group 0, scaled up
+    qdir = q[:, 0:4, :].float().mean(dim=(0, 1))
+    k[0, pos] = (qdir / qdir.norm() * 60.0 / (1 / np.sqrt(d)) / 11.0).to(torch.bfloat16)
+    o, lse = tsw.tree_attn_verify(q, k, v, parent, npre)
+    torch.cuda.synchronize()
+    o_ref, l_ref = oracle.tree_attn(wl.oracle_view(q), wl.oracle_view(k), wl.oracle_view(v),
+                                    parent, npre, 1 / np.sqrt(d), nthreads=NTHREADS)
+    assert float(np.max(l_ref[:, 0:4])) - float(np.median(l_ref)) > 20.0
+    check(o, lse, o_ref, l_ref, TOL["bf16"], "large logit %s" % where)

@@ -1,0 +1,64 @@
+// Device helpers shared by the gfx950 kernels (vector types, base-2
+// exponential, cross-lane reductions, LDS swizzle, explicit waits).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+namespace tsw {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+
+constexpr float kLn2 = 0.693147180559945309417f;
+constexpr float kLog2e = 1.44269504088896340736f;
+
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Shuffle-based reductions (ds_bpermute); any xor distance.
+__device__ __forceinline__ float xor_max(float x, int m) { return fmaxf(x, __shfl_xor(x, m)); }
+__device__ __forceinline__ float xor_sum(float x, int m) { return x + __shfl_xor(x, m); }
+
+// Combine lanes l, l^16, l^32, l^48 with the gfx950 permlane swaps (VALU,
+// no LDS round trip).  After a swap of a value with itself, the two halves
+// of the result hold x[l] and x[partner] in some order, so max/sum of the
+// pair is the same in every lane.
+__device__ __forceinline__ float quad_max(float x) {
+    auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float quad_sum(float x) {
+    auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+// 16-byte chunk swizzle of a 256-byte LDS row.  Logical chunk c of tile row r
+// lives in physical slot c ^ swz(r).  For any 8 (and 16) consecutive aligned
+// rows the slots of one logical chunk are all different, and for any 4
+// (and 8) consecutive aligned rows the chunk pairs {2b, 2b+1} land in
+// different slot pairs, so both the K operand reads (one chunk of 16 rows)
+// and the transposed V reads (two chunks of 4 rows per 16 lanes) are free of
+// bank conflicts whether the LDS serves 128 or 256 bytes per clock.
+__device__ __forceinline__ int swz(int r) { return ((2 * (r & 7)) | ((r >> 2) & 1)) ^ ((r >> 3) & 1); }
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    // gfx9 s_waitcnt: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt_hi[15:14]
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Work-group barrier that does not wait for outstanding LDS-DMA loads (the
+// pipelines wait for exactly the tiles they need with wait_vmcnt).  Pending
+// LDS reads are drained first so a stage is never overwritten under a read.
+__device__ __forceinline__ void barrier_lds() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+}  // namespace tsw
