@@ -272,8 +272,12 @@ def test_non_ancestor_tree_rows_do_not_leak():
     k2[:, [npre + j for j in others], :] = 1e4
     o2, l2 = tsw.tree_attn_verify(q, k2, v, parent, npre)
     torch.cuda.synchronize()
-    assert torch.equal(o1[39], o2[39]) and torch.equal(l1[39], l2[39])
-    assert torch.equal(o1[0], o2[0]) and torch.equal(l1[0], l2[0])
+    # Nodes 39 and 0 see none of the poisoned rows.  (The poisoned scores can
+    # send the work-group through the exact two-pass path, so the unaffected
+    # rows may differ by rounding, not by more.)
+    for node in (39, 0):
+        assert float((o1[node] - o2[node]).abs().max()) <= 1e-4
+        assert float((l1[node] - l2[node]).abs().max()) <= 1e-4
     # nodes that do see poisoned rows change; all rows must match the oracle
     o_ref, l_ref = oracle.tree_attn(wl.oracle_view(q), wl.oracle_view(k2), wl.oracle_view(v),
                                     parent, npre, 1 / np.sqrt(d), nthreads=NTHREADS)
@@ -355,12 +359,16 @@ def test_large_logit_headroom(where):
     k = gen((Hkv, npre + T, d), 82, torch.bfloat16)
     v = gen((Hkv, npre + T, d), 83, torch.bfloat16)
     pos = {"first_tile": 0, "late_tile": 3000, "tree_row": npre + 7}[where]
-    # K row aligned with the mean query direction of head group 0, scaled up
-    qdir = q[:, 0:4, :].float().mean(dim=(0, 1))
-    k[0, pos] = (qdir / qdir.norm() * 60.0 / (1 / np.sqrt(d)) / 11.0).to(torch.bfloat16)
+    # every query of head 0 is the same vector u; one key of kv head 0 is
+    # 10.5 u, so that key scores 10.5 |u|^2 / sqrt(d) ~ 60 nats for all of them
+    u = gen((d,), 84, torch.float32)
+    u = (u / u.norm() * 8.0).to(torch.bfloat16)
+    q[:, 0, :] = u
+    k[0, pos] = (u.float() * 10.5).to(torch.bfloat16)
     o, lse = tsw.tree_attn_verify(q, k, v, parent, npre)
     torch.cuda.synchronize()
     o_ref, l_ref = oracle.tree_attn(wl.oracle_view(q), wl.oracle_view(k), wl.oracle_view(v),
                                     parent, npre, 1 / np.sqrt(d), nthreads=NTHREADS)
-    assert float(np.max(l_ref[:, 0:4])) - float(np.median(l_ref)) > 20.0
+    if where != "tree_row":
+        assert float(np.min(l_ref[:, 0])) - float(np.median(l_ref)) > 45.0
     check(o, lse, o_ref, l_ref, TOL["bf16"], "large logit %s" % where)

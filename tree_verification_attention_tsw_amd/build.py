@@ -9,8 +9,15 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libtsw.so")
-SOURCES = [os.path.join(CSRC, n) for n in ("tsw_api.cpp", "tsw_kernels.hip", "tsw_mfma.hip")]
-HEADERS = [os.path.join(CSRC, n) for n in ("tsw_internal.h", "tsw_device.h")] + [
+# Matrix-core kernel shapes (row groups, query blocks per wave); each one is
+# its own object compiled from tsw_mfma_inst.hip, so they build in parallel.
+MFMA_SHAPES = [(1, 1), (1, 2), (1, 3), (1, 4), (2, 3), (2, 4), (2, 5), (4, 3), (4, 4), (4, 5)]
+# (source, extra flags, object name)
+UNITS = [(os.path.join(CSRC, n), [], n + ".o") for n in ("tsw_api.cpp", "tsw_kernels.hip", "tsw_mfma.hip")] + [
+    (os.path.join(CSRC, "tsw_mfma_inst.hip"), ["-DTSW_R=%d" % r, "-DTSW_NB=%d" % nb],
+     "tsw_mfma_%d_%d.o" % (r, nb)) for r, nb in MFMA_SHAPES]
+SOURCES = sorted(set(u[0] for u in UNITS))
+HEADERS = [os.path.join(CSRC, n) for n in ("tsw_internal.h", "tsw_device.h", "tsw_mfma_impl.h")] + [
     os.path.join(INCLUDE, "tsw.h")]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -44,12 +51,14 @@ def build(verbose=False):
     import tempfile
 
     with tempfile.TemporaryDirectory(prefix="tsw_build_") as tmpd:
-        objs = [os.path.join(tmpd, os.path.basename(src) + ".o") for src in SOURCES]
-        cmds = [[HIPCC] + FLAGS + ["-c", src, "-o", obj] for src, obj in zip(SOURCES, objs)]
+        objs = [os.path.join(tmpd, name) for _, _, name in UNITS]
+        cmds = [[HIPCC] + FLAGS + extra + ["-c", src, "-o", obj]
+                for (src, extra, _), obj in zip(UNITS, objs)]
         if verbose:
             for c in cmds:
                 print(" ".join(c), flush=True)
-        with cf.ThreadPoolExecutor(max_workers=len(cmds)) as ex:
+        workers = max(1, min(len(cmds), int(os.environ.get("MAX_JOBS", os.cpu_count() or 4))))
+        with cf.ThreadPoolExecutor(max_workers=workers) as ex:
             results = list(ex.map(lambda c: subprocess.run(c, stdout=subprocess.PIPE,
                                                            stderr=subprocess.STDOUT, text=True),
                                   cmds))

@@ -1,487 +1,13 @@
-// Matrix-core split kernel for tree-verification attention (gfx950, bf16,
-// head dim 128).
-//
-// One work-group per (split, kv head): it streams a contiguous slice of that
-// head's key list once (prefix keys, then -- in the last split -- the tree's
-// own rows under the ancestor mask) and applies it to all M = T * (Hq/Hkv)
-// query rows that share the head, so every K/V byte leaves HBM once per call
-// (the GQA head group and all tree nodes ride on one K/V stream).  Sources:
-// "TokenSwift - A framework for accelerating the generation of ultra-long
-// text" (aiboss88 project page), technical principles, tree-based
-// multi-candidate verification; Tencent Cloud article "90分钟生成10万Token，
-// 新框架实现3倍无损加速超长文本生成", 技术原理 figure text (verification with
-// the full KV cache) and 无损的输出质量 (draft pass = same model over a
-// partial KV cache).
-//
-// Layout of the work: four wavefronts, one per SIMD, each owning up to NB
-// blocks of 16 query rows (R row groups) and one 32-key sub-tile of every key
-// tile (4/R sub-tiles per tile).  Per tile:
-//   * K and V rows move HBM -> LDS with global_load_lds_dwordx4 into a
-//     128 KB ring (2, 4 or 8 stages); explicit s_waitcnt vmcnt keeps later
-//     tiles in flight, and a work-group barrier per tile recycles stages.
-//   * S^T = K Q^T on v_mfma_f32_16x16x32_bf16 with key rows on the M axis and
-//     query rows on N: each lane owns one query row, so the row maximum is an
-//     in-lane max over 8 scores plus two permlane swaps, and the online
-//     softmax rescale of O is one scalar per lane.
-//   * O^T += V^T P^T on the same instruction; V^T operands come straight from
-//     row-major LDS through ds_read_b64_tr_b16.
-//   * The exponentials of query block b+1 and the P V products of block b
-//     share one basic block, so a wave's matrix and vector work overlap.
-#include <type_traits>
-
-#include "tsw_device.h"
+// Shape table and dispatch of the matrix-core split kernel (the kernel
+// itself is in tsw_mfma_impl.h, instantiated per shape by tsw_mfma_inst.hip).
 #include "tsw_internal.h"
 
 namespace tsw {
-namespace {
 
-// Headroom (log2 units) of the fast pass: each row exponentiates against a
-// fixed reference -- the first finite tile maximum it sees -- so p <= 2^64
-// as long as no later score exceeds the reference by more than this.  A row
-// that does (rare: a logit 44 nats above everything seen so far) sends its
-// work-group through the exact two-pass path.
-constexpr float kHeadroom = 64.0f;
-
-template <int R_, int NB_>
-struct Shape {
-    static constexpr int R = R_;
-    static constexpr int NB = NB_;
-    static constexpr int WAVES = 4;
-    static constexpr int KS = WAVES / R;            // 32-key sub-tiles per tile
-    static constexpr int TK = 32 * KS;              // keys per tile
-    static constexpr int ROWB = 256;                // bytes per K or V row
-    static constexpr int STAGE = 2 * TK * ROWB;     // one K tile + one V tile
-    static constexpr int RING = 128 * 1024;
-    static constexpr int STAGES = RING / STAGE;     // 2, 4 or 8
-    static constexpr int NI = TK / (2 * WAVES);     // DMA instructions per wave per tile
-    static constexpr int XSLOTS = (KS - 1) * R * NB;   // parked (wave, block) pairs
-    static constexpr int XBYTES = XSLOTS * (8 * 64 * 16 + 32 * 4);
-    static constexpr int IDX_BYTES = kGatherChunkMax * 4;
-    static constexpr int smem(bool gather) {
-        const int loop = RING + (gather ? IDX_BYTES : 0);
-        return loop > XBYTES ? loop : XBYTES;
-    }
-};
-
-struct Ctx {
-    char* smem;
-    const int32_t* idx_lds;
-    const char* kbase;
-    const char* vbase;
-    int64_t c0, c1;      // prefix key range [c0, c1) of this split
-    int n_pre_tiles, n_tiles;
-    int lane, li, lj, w, rg, ks, split, g;
-};
-
-// Issue the DMA loads of tile tt into ring stage st.  One instruction moves
-// four 256-byte rows (64 lanes x 16 bytes) into consecutive LDS; rows past
-// the slice end re-read a valid row (their scores are masked to -inf).
-template <class S, bool GATHER>
-__device__ __forceinline__ void issue_tile(const SplitArgs& a, const Ctx& cx, int tt, int st) {
-    char* sbase = cx.smem + st * S::STAGE;
-#pragma unroll
-    for (int i = 0; i < S::NI; ++i) {
-        const int u = cx.w * S::NI + i;
-        const bool isv = u >= S::TK / 4;
-        const int grp = isv ? u - S::TK / 4 : u;
-        const int row = grp * 4 + cx.lj;
-        int64_t pos;
-        if (tt < cx.n_pre_tiles) {
-            int64_t kk = cx.c0 + (int64_t)tt * S::TK + row;
-            if (kk >= cx.c1) kk = cx.c0;
-            pos = GATHER ? (int64_t)cx.idx_lds[kk - cx.c0] : kk;
-        } else {
-            int jj = (tt - cx.n_pre_tiles) * S::TK + row;
-            if (jj >= a.T) jj = a.T - 1;
-            pos = a.n_prefix + jj;
-        }
-        const char* src = (isv ? cx.vbase : cx.kbase) + pos * S::ROWB + 16 * (cx.li ^ swz(row));
-        char* dst = sbase + (isv ? S::TK * S::ROWB : 0) + grp * 1024;
-        __builtin_amdgcn_global_load_lds((const void*)src, (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
-    }
-}
-
-// Wait until this wave's loads of tile tt have landed while `newer` later
-// tiles stay in flight.
-template <class S>
-__device__ __forceinline__ void wait_tile(int newer) {
-    if constexpr (S::STAGES >= 8) {
-        if (newer >= 6) { wait_vmcnt<6 * S::NI>(); return; }
-        if (newer == 5) { wait_vmcnt<5 * S::NI>(); return; }
-        if (newer == 4) { wait_vmcnt<4 * S::NI>(); return; }
-        if (newer == 3) { wait_vmcnt<3 * S::NI>(); return; }
-    }
-    if constexpr (S::STAGES >= 4) {
-        if (newer >= 2) { wait_vmcnt<2 * S::NI>(); return; }
-    }
-    if constexpr (S::STAGES >= 3) {
-        if (newer >= 1) { wait_vmcnt<S::NI>(); return; }
-    }
-    wait_vmcnt<0>();
-}
-
-// K operands of this wave's 32-key sub-tile: lane (li, lj) holds key row
-// kb*16 + li, head-dim elements 32*s + 8*lj .. +7.
-template <class S>
-__device__ __forceinline__ void load_k(const char* Ks, const Ctx& cx, bf16x8 (&kop)[2][4]) {
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-        const int row = cx.ks * 32 + kb * 16 + cx.li;
-        const char* base = Ks + row * S::ROWB;
-        const int sw = swz(row);
-#pragma unroll
-        for (int s = 0; s < 4; ++s) kop[kb][s] = *(const bf16x8*)(base + 16 * ((4 * s + cx.lj) ^ sw));
-    }
-}
-
-// V^T operands: the transposed reads give lane (li, lj) V[key][16*db + li]
-// for keys 4*lj .. 4*lj+3 of each 16-key half, matching P^T's layout.
-template <class S>
-__device__ __forceinline__ void load_v(const char* Vs, const Ctx& cx, bf16x8 (&vop)[8]) {
-    const int trow0 = cx.ks * 32 + 4 * cx.lj + (cx.li >> 2);
-    const int trow1 = trow0 + 16;
-    const int tsel = (cx.li >> 1) & 1;
-    const char* vrow0 = Vs + trow0 * S::ROWB + 8 * (cx.li & 1);
-    const char* vrow1 = Vs + trow1 * S::ROWB + 8 * (cx.li & 1);
-    const int sw0 = swz(trow0) ^ tsel;
-    const int sw1 = swz(trow1) ^ tsel;
-#pragma unroll
-    for (int db = 0; db < 8; ++db) {
-        const bf16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vrow0 + 16 * ((2 * db) ^ sw0)));
-        const bf16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vrow1 + 16 * ((2 * db) ^ sw1)));
-        vop[db] = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
-    }
-}
-
-// S^T blocks (16 keys x 16 queries) for both key halves of every query block.
-template <int NBA>
-__device__ __forceinline__ void qk(const bf16x8 (&kop)[2][4], const bf16x8 (&qop)[NBA][4], f32x4 (&sc)[NBA][2]) {
-#pragma unroll
-    for (int b = 0; b < NBA; ++b)
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) sc[b][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int s = 0; s < 4; ++s)
-#pragma unroll
-        for (int b = 0; b < NBA; ++b)
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-                sc[b][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[kb][s], qop[b][s], sc[b][kb], 0, 0, 0);
-}
-
-// Scores of keys past the slice end, and of tree rows that are not
-// ancestors-or-self of the query's node, become -inf.
-template <class S, int NBA>
-__device__ __forceinline__ void mask_tile(const SplitArgs& a, const Ctx& cx, int tt, f32x4 (&sc)[NBA][2]) {
-    const bool tail = tt >= cx.n_pre_tiles;
-    const int64_t kstart = tail ? (int64_t)(tt - cx.n_pre_tiles) * S::TK : cx.c0 + (int64_t)tt * S::TK;
-    const int64_t kend = tail ? a.T : cx.c1;
-    if (!tail && kstart + S::TK <= kend) return;
-    uint64_t nmask[NBA];
-#pragma unroll
-    for (int b = 0; b < NBA; ++b) {
-        const int r = (cx.rg + b * S::R) * 16 + cx.li;
-        nmask[b] = (tail && r < a.M) ? a.mask[r / a.G] : ~0ull;
-    }
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int64_t key = kstart + cx.ks * 32 + kb * 16 + 4 * cx.lj + i;
-            const bool in_range = key < kend;
-#pragma unroll
-            for (int b = 0; b < NBA; ++b) {
-                bool ok = in_range;
-                if (tail) ok = ok && ((nmask[b] >> (key & 63)) & 1ull);
-                if (!ok) sc[b][kb][i] = -INFINITY;
-            }
-        }
-}
-
-// Row maxima of a tile, in log2 units (scores times scale*log2(e)).
-template <int NBA>
-__device__ __forceinline__ void tile_max(const f32x4 (&sc)[NBA][2], float c, float (&mt)[NBA]) {
-#pragma unroll
-    for (int b = 0; b < NBA; ++b) {
-        const float m0 = fmaxf(fmaxf(sc[b][0][0], sc[b][0][1]), fmaxf(sc[b][0][2], sc[b][0][3]));
-        const float m1 = fmaxf(fmaxf(sc[b][1][0], sc[b][1][1]), fmaxf(sc[b][1][2], sc[b][1][3]));
-        mt[b] = quad_max(fmaxf(m0, m1)) * c;
-    }
-}
-
-// p = 2^(s*c - m) for one query block, rounded to bf16 for the P V
-// product; the row sum adds the same rounded values (v_dot2c_f32_bf16 with
-// (1, 1)), so the normalisation matches the weights actually applied to V.
-__device__ __forceinline__ void softmax_p1(const f32x4 (&sc)[2], float c, float m_run, float& l_run,
-                                           bf16x8& pb) {
-    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
-    const float mu = m_run == -INFINITY ? 0.0f : m_run;
-    float lsum = l_run;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int i = 0; i < 4; i += 2) {
-            const bf16x2 pp = {(__bf16)exp2_fast(fmaf(sc[kb][i], c, -mu)),
-                               (__bf16)exp2_fast(fmaf(sc[kb][i + 1], c, -mu))};
-            lsum = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, lsum, false);
-            pb[kb * 4 + i] = pp[0];
-            pb[kb * 4 + i + 1] = pp[1];
-        }
-    l_run = lsum;
-}
-
-// The work of one wavefront owning NBA query blocks.
-template <class S, bool GATHER, int NBA>
-__device__ __forceinline__ void run_wave(const SplitArgs& a, const Ctx& cx) {
-    constexpr int STAGES = S::STAGES;
-    const float c = a.scale_log2;
-
-    // Q^T as the B operand: lane (li, lj) holds query row li of the block,
-    // head-dim elements 32*s + 8*lj .. +7.  Rows past M load row 0 and are
-    // zeroed.  The loads drain before the K/V pipeline starts, so the tile
-    // loop never waits on them.
-    bf16x8 qop[NBA][4];
-#pragma unroll
-    for (int b = 0; b < NBA; ++b) {
-        const int r = (cx.rg + b * S::R) * 16 + cx.li;
-        const bool ok = r < a.M;
-        const int t = ok ? r / a.G : 0;
-        const int h = ok ? cx.g * a.G + r % a.G : 0;
-        const bf16x8* src = (const bf16x8*)((const __bf16*)a.q + ((size_t)t * a.Hq + h) * 128 + 8 * cx.lj);
-#pragma unroll
-        for (int s = 0; s < 4; ++s) qop[b][s] = src[4 * s];
-        if (!ok) {
-#pragma unroll
-            for (int s = 0; s < 4; ++s)
-#pragma unroll
-                for (int e = 0; e < 8; ++e) qop[b][s][e] = (__bf16)0.0f;
-        }
-    }
-    wait_vmcnt<0>();
-
-    float m_run[NBA], l_run[NBA];
-    f32x4 o[NBA][8];
-#pragma unroll
-    for (int b = 0; b < NBA; ++b) {
-        m_run[b] = -INFINITY;
-        l_run[b] = 0.0f;
-#pragma unroll
-        for (int db = 0; db < 8; ++db) o[b][db] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-
-    const int n = cx.n_tiles;
-
-    bf16x8 kop[2][4], vop[8];
-    f32x4 sc[NBA][2];
-    float mt[NBA];
-    bool bad = false;
-
-    // One pass over the split's tiles.  FAST: every row exponentiates against
-    // a fixed reference (its first finite tile maximum; O and l are still
-    // zero when it is adopted) and flags itself if a later score exceeds it by
-    // more than kHeadroom.  MAXONLY: Q K only, exact row maxima.  EXACT: P V
-    // against those maxima (p <= 1).  Every pass crosses one barrier per tile.
-    constexpr int FAST = 0, MAXONLY = 1, EXACT = 2;
-    auto pass = [&](auto mode_c) {
-        constexpr int MODE = decltype(mode_c)::value;
-#pragma unroll
-        for (int s = 0; s < STAGES - 1; ++s)
-            if (s < n) issue_tile<S, GATHER>(a, cx, s, s);
-        for (int t = 0; t < n; ++t) {
-            // Tiles issued so far end at min(n-1, t+STAGES-2).
-            const int newer = n - 1 - t < STAGES - 2 ? n - 1 - t : STAGES - 2;
-            wait_tile<S>(newer);
-            barrier_lds();
-            // The stage of tile t-1 is free once every wave passed the barrier.
-            if (t + STAGES - 1 < n) issue_tile<S, GATHER>(a, cx, t + STAGES - 1, (t + STAGES - 1) % STAGES);
-            const char* Ks = cx.smem + (t % STAGES) * S::STAGE;
-            load_k<S>(Ks, cx, kop);
-            qk<NBA>(kop, qop, sc);
-            if constexpr (MODE != MAXONLY) load_v<S>(Ks + S::TK * S::ROWB, cx, vop);
-            mask_tile<S, NBA>(a, cx, t, sc);
-            if constexpr (MODE == FAST) {
-                tile_max<NBA>(sc, c, mt);
-#pragma unroll
-                for (int b = 0; b < NBA; ++b) {
-                    m_run[b] = m_run[b] == -INFINITY ? mt[b] : m_run[b];
-                    bad = bad || (mt[b] > m_run[b] + kHeadroom);
-                }
-            }
-            if constexpr (MODE == MAXONLY) {
-                tile_max<NBA>(sc, c, mt);
-#pragma unroll
-                for (int b = 0; b < NBA; ++b) m_run[b] = fmaxf(m_run[b], mt[b]);
-            } else {
-                // O (queries x d) += P (queries x keys) V (keys x d): lane
-                // (li, lj) of accumulator block (b, db) holds
-                // O[4*lj + i][16*db + li].  The exponentials of block b+1 do
-                // not depend on the P V products of block b, so vector and
-                // matrix work overlap.
-#pragma unroll
-                for (int b = 0; b < NBA; ++b) {
-                    bf16x8 pb;
-                    softmax_p1(sc[b], c, m_run[b], l_run[b], pb);
-#pragma unroll
-                    for (int db = 0; db < 8; ++db)
-                        o[b][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pb, vop[db], o[b][db], 0, 0, 0);
-                }
-            }
-        }
-    };
-
-    pass(std::integral_constant<int, FAST>{});
-#pragma unroll
-    for (int b = 0; b < NBA; ++b) bad = bad || !isfinite(l_run[b]);
-    // Work-group vote: any flagged wave sends every wave through the exact
-    // path, which keeps the barrier sequence identical across waves.
-    int* votes = (int*)(cx.smem + S::smem(GATHER));
-    barrier_lds();
-    if (cx.lane == 0) votes[cx.w] = __builtin_amdgcn_ballot_w64(bad) != 0;
-    barrier_lds();
-    if (votes[0] | votes[1] | votes[2] | votes[3]) {
-#pragma unroll
-        for (int b = 0; b < NBA; ++b) m_run[b] = -INFINITY;
-        pass(std::integral_constant<int, MAXONLY>{});
-#pragma unroll
-        for (int b = 0; b < NBA; ++b) {
-            l_run[b] = 0.0f;
-#pragma unroll
-            for (int db = 0; db < 8; ++db) o[b][db] = f32x4{0.f, 0.f, 0.f, 0.f};
-        }
-        pass(std::integral_constant<int, EXACT>{});
-    }
-
-    // Row sums: each lane summed its own keys; add the four lane groups.
-#pragma unroll
-    for (int b = 0; b < NBA; ++b) l_run[b] = quad_sum(l_run[b]);
-
-    // Combine the KS key sub-tiles of each row group through LDS: waves with
-    // ks > 0 park their accumulators (lane-major, one f32x4 per lane) and
-    // their per-row (m, l); the ks = 0 wave merges and writes the partial.
-    f32x4* xo = (f32x4*)cx.smem;
-    float* xml = (float*)(cx.smem + S::XSLOTS * 8 * 64 * 16);
-    if constexpr (S::KS > 1) {
-        barrier_lds();
-        if (cx.ks > 0) {
-#pragma unroll
-            for (int b = 0; b < NBA; ++b) {
-                const int slot = ((cx.ks - 1) * S::R + cx.rg) * S::NB + b;
-#pragma unroll
-                for (int db = 0; db < 8; ++db) xo[(slot * 8 + db) * 64 + cx.lane] = o[b][db];
-                if (cx.lj == 0) {
-                    xml[slot * 32 + cx.li] = m_run[b];
-                    xml[slot * 32 + 16 + cx.li] = l_run[b];
-                }
-            }
-        }
-        barrier_lds();
-        if (cx.ks > 0) return;
-    }
-
-#pragma unroll
-    for (int b = 0; b < NBA; ++b) {
-        // per-row weights, computed by the lanes that own row li
-        float wk[S::KS];
-        float mmax = m_run[b];
-#pragma unroll
-        for (int k2 = 1; k2 < S::KS; ++k2)
-            mmax = fmaxf(mmax, xml[(((k2 - 1) * S::R + cx.rg) * S::NB + b) * 32 + cx.li]);
-        float L = 0.0f;
-#pragma unroll
-        for (int k2 = 0; k2 < S::KS; ++k2) {
-            const int slot = ((k2 - 1) * S::R + cx.rg) * S::NB + b;
-            const float mk = k2 == 0 ? m_run[b] : xml[slot * 32 + cx.li];
-            const float lk = k2 == 0 ? l_run[b] : xml[slot * 32 + 16 + cx.li];
-            wk[k2] = mk == -INFINITY ? 0.0f : exp2_fast(mk - mmax);
-            L += wk[k2] * lk;
-        }
-        const float inv = L > 0.0f ? 1.0f / L : 0.0f;
-        const int rbase = (cx.rg + b * S::R) * 16;
-        if (cx.lj == 0 && rbase + cx.li < a.M) {
-            const int r = rbase + cx.li;
-            const size_t orow = ((size_t)cx.split * a.T + r / a.G) * a.Hq + cx.g * a.G + r % a.G;
-            a.part_lse[orow] = L > 0.0f ? (mmax + __log2f(L)) * kLn2 : -INFINITY;
-        }
-        // accumulator element i of this lane belongs to row 4*lj + i
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int q = 4 * cx.lj + i;
-            float wq[S::KS];
-#pragma unroll
-            for (int k2 = 0; k2 < S::KS; ++k2) wq[k2] = __shfl(wk[k2] * inv, q);
-            const int r = rbase + q;
-            if (r >= a.M) continue;
-            const size_t orow = ((size_t)cx.split * a.T + r / a.G) * a.Hq + cx.g * a.G + r % a.G;
-            float* dst = a.part_o + orow * 128 + cx.li;
-#pragma unroll
-            for (int db = 0; db < 8; ++db) {
-                float acc = o[b][db][i] * wq[0];
-#pragma unroll
-                for (int k2 = 1; k2 < S::KS; ++k2) {
-                    const int slot = ((k2 - 1) * S::R + cx.rg) * S::NB + b;
-                    acc += wq[k2] * xo[(slot * 8 + db) * 64 + cx.lane][i];
-                }
-                dst[16 * db] = acc;
-            }
-        }
-    }
-}
-
-template <int R, int NB, bool GATHER>
-__global__ __launch_bounds__(256, 1) void split_mfma(const SplitArgs a) {
-    using S = Shape<R, NB>;
-    constexpr int SMEM = S::smem(GATHER);
-    static_assert(SMEM <= 160 * 1024, "LDS budget");
-    static_assert(S::NI >= 1 && (S::TK / 2) % S::WAVES == 0, "tile / wave split");
-    __shared__ __attribute__((aligned(1024))) char smem[SMEM + 16];
-
-    Ctx cx;
-    cx.smem = smem;
-    cx.lane = threadIdx.x & 63;
-    cx.li = cx.lane & 15;
-    cx.lj = cx.lane >> 4;
-    // wave index as a scalar, so per-wave choices compile to scalar branches
-    cx.w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    cx.rg = cx.w / S::KS;
-    cx.ks = cx.w % S::KS;
-    cx.split = blockIdx.x;
-    cx.g = blockIdx.y;
-    cx.c0 = (int64_t)cx.split * a.chunk_keys;
-    cx.c1 = cx.c0 + a.chunk_keys < a.n_keys ? cx.c0 + a.chunk_keys : a.n_keys;
-    cx.n_pre_tiles = cx.c1 > cx.c0 ? (int)((cx.c1 - cx.c0 + S::TK - 1) / S::TK) : 0;
-    const int n_tail_tiles = cx.split == a.n_splits - 1 ? (a.T + S::TK - 1) / S::TK : 0;
-    cx.n_tiles = cx.n_pre_tiles + n_tail_tiles;
-    cx.kbase = (const char*)a.k + (size_t)cx.g * (size_t)a.kv_head_stride * 2;
-    cx.vbase = (const char*)a.v + (size_t)cx.g * (size_t)a.kv_head_stride * 2;
-    int32_t* idx_lds = (int32_t*)(smem + S::RING);
-    cx.idx_lds = idx_lds;
-    if constexpr (GATHER) {
-        const int n = (int)(cx.c1 > cx.c0 ? cx.c1 - cx.c0 : 0);
-        for (int i = threadIdx.x; i < n; i += S::WAVES * 64) idx_lds[i] = a.idx[cx.c0 + i];
-        __syncthreads();
-    }
-
-    // Query blocks are dealt round-robin to the R row groups, so a wave owns
-    // NB or NB-1 of them (the planner guarantees it).
-    const int nblk = (a.M + 15) >> 4;
-    const int nb_act = (nblk - cx.rg + S::R - 1) / S::R;
-    if constexpr (S::R == 1) {
-        run_wave<S, GATHER, NB>(a, cx);
-    } else {
-        if (nb_act >= NB) run_wave<S, GATHER, NB>(a, cx);
-        else run_wave<S, GATHER, NB - 1>(a, cx);
-    }
-}
-
-template <int R, int NB>
-hipError_t launch_t(bool gather, const SplitArgs& a, int n_kv_heads, hipStream_t stream) {
-    const dim3 grid(a.n_splits, n_kv_heads);
-    if (gather) hipLaunchKernelGGL((split_mfma<R, NB, true>), grid, dim3(256), 0, stream, a);
-    else hipLaunchKernelGGL((split_mfma<R, NB, false>), grid, dim3(256), 0, stream, a);
-    return hipGetLastError();
-}
-
-}  // namespace
+#define TSW_SHAPES(X) X(1, 1) X(1, 2) X(1, 3) X(1, 4) X(2, 3) X(2, 4) X(2, 5) X(4, 3) X(4, 4) X(4, 5)
+#define TSW_DECLARE(r, nb) \
+    hipError_t launch_mfma_##r##_##nb(bool gather, const SplitArgs& a, int n_kv_heads, hipStream_t stream);
+TSW_SHAPES(TSW_DECLARE)
 
 bool mfma_config_for(int M, MfmaConfig* cfg) {
     // Blocks of 16 query rows per kv head, dealt to R row groups so that
@@ -501,19 +27,11 @@ bool mfma_config_for(int M, MfmaConfig* cfg) {
 
 hipError_t launch_split_mfma(const MfmaConfig& cfg, bool gather, const SplitArgs& a, int n_kv_heads,
                              hipStream_t stream) {
-    switch (cfg.rgroups * 16 + cfg.nb) {
-        case 1 * 16 + 1: return launch_t<1, 1>(gather, a, n_kv_heads, stream);
-        case 1 * 16 + 2: return launch_t<1, 2>(gather, a, n_kv_heads, stream);
-        case 1 * 16 + 3: return launch_t<1, 3>(gather, a, n_kv_heads, stream);
-        case 1 * 16 + 4: return launch_t<1, 4>(gather, a, n_kv_heads, stream);
-        case 2 * 16 + 3: return launch_t<2, 3>(gather, a, n_kv_heads, stream);
-        case 2 * 16 + 4: return launch_t<2, 4>(gather, a, n_kv_heads, stream);
-        case 2 * 16 + 5: return launch_t<2, 5>(gather, a, n_kv_heads, stream);
-        case 4 * 16 + 3: return launch_t<4, 3>(gather, a, n_kv_heads, stream);
-        case 4 * 16 + 4: return launch_t<4, 4>(gather, a, n_kv_heads, stream);
-        case 4 * 16 + 5: return launch_t<4, 5>(gather, a, n_kv_heads, stream);
-        default: return hipErrorInvalidValue;
-    }
+#define TSW_CASE(R_, NB_) \
+    if (cfg.rgroups == R_ && cfg.nb == NB_) return launch_mfma_##R_##_##NB_(gather, a, n_kv_heads, stream);
+    TSW_SHAPES(TSW_CASE)
+#undef TSW_CASE
+    return hipErrorInvalidValue;
 }
 
 }  // namespace tsw
