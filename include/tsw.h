@@ -75,7 +75,9 @@ enum {
 enum { TSW_DTYPE_F32 = 0, TSW_DTYPE_BF16 = 1 };
 
 /* Kernel family choice.  AUTO takes the matrix-core (MFMA) kernel for
- * bfloat16 with d = 128 and shapes it covers, else the vector-ALU kernel. */
+ * bfloat16 with d = 128, at most 384 query rows T * (Hq / Hkv) per kv head
+ * and at least 256 keys, else the vector-ALU kernel.  MFMA outside its
+ * shapes returns TSW_EUNSUPPORTED. */
 enum { TSW_IMPL_AUTO = 0, TSW_IMPL_VALU = 1, TSW_IMPL_MFMA = 2 };
 
 /* A cache stream handle: a hipStream_t (NULL = the legacy default stream). */

@@ -114,8 +114,8 @@ def test_desc_errors(L, field, value, code):
 def test_mfma_forced_on_unsupported_shape(L):
     # float32 inputs have no matrix-core kernel here
     assert _verify(L, _desc(impl=2, dtype=tsw.DTYPE_F32)) == EUNSUP
-    # more than 20 query blocks of 16 rows per kv head
-    assert _verify(L, _desc(impl=2, T=64, Hq=48, Hkv=8, d=128,
+    # more than 24 query blocks of 16 rows (384 rows) per kv head
+    assert _verify(L, _desc(impl=2, T=64, Hq=56, Hkv=8, d=128,
                             kv_head_stride=(100 + 64) * 128),
                    parent=np.ascontiguousarray(wl.kary_tree_parent(64, 3))) == EUNSUP
 

@@ -152,10 +152,12 @@ def test_workload_partial32_layers():
 # ------------------------------------------------------------ shapes / edges
 
 # Query rows per kv head M = T * G select the matrix-core shape (blocks of 16
-# rows: 1-2, 3-4, 5-8, 9-12, 13-16); each shape is covered, with ragged M.
+# rows: 1-2, 3-4, 5-8, 9-12, 13-16, 17-24); each shape is covered, with
+# ragged M and with row groups that own one block fewer than the others.
 MFMA_SHAPES = [
     (1, 1, 1), (13, 1, 1), (16, 2, 1), (4, 8, 8), (40, 1, 1), (13, 4, 1), (40, 2, 1),
-    (33, 4, 1), (40, 4, 1), (47, 4, 1), (64, 3, 1), (40, 5, 1), (64, 4, 1), (61, 4, 1),
+    (23, 4, 1), (40, 3, 1), (33, 4, 1), (40, 4, 1), (47, 4, 1), (64, 3, 1), (40, 5, 1),
+    (64, 4, 1), (61, 4, 1), (53, 5, 1), (50, 7, 1), (64, 6, 2),
 ]
 
 

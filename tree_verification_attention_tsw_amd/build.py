@@ -9,13 +9,15 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libtsw.so")
-# Matrix-core kernel shapes (row groups, query blocks per wave); each one is
-# its own object compiled from tsw_mfma_inst.hip, so they build in parallel.
-MFMA_SHAPES = [(1, 1), (1, 2), (1, 3), (1, 4), (2, 3), (2, 4), (2, 5), (4, 3), (4, 4), (4, 5)]
+# Matrix-core kernel shapes (waves, row groups, query blocks per wave); each
+# one is its own object compiled from tsw_mfma_inst.hip, so they build in
+# parallel.
+MFMA_SHAPES = [(4, 1, 1), (4, 1, 2), (4, 1, 3), (4, 1, 4), (4, 2, 3), (4, 2, 4), (4, 2, 5), (4, 4, 3), (4, 4, 4),
+               (4, 4, 5), (8, 2, 2), (8, 4, 2), (8, 4, 3), (8, 8, 2), (8, 8, 3)]
 # (source, extra flags, object name)
 UNITS = [(os.path.join(CSRC, n), [], n + ".o") for n in ("tsw_api.cpp", "tsw_kernels.hip", "tsw_mfma.hip")] + [
-    (os.path.join(CSRC, "tsw_mfma_inst.hip"), ["-DTSW_R=%d" % r, "-DTSW_NB=%d" % nb],
-     "tsw_mfma_%d_%d.o" % (r, nb)) for r, nb in MFMA_SHAPES]
+    (os.path.join(CSRC, "tsw_mfma_inst.hip"), ["-DTSW_W=%d" % w, "-DTSW_R=%d" % r, "-DTSW_NB=%d" % nb],
+     "tsw_mfma_%d_%d_%d.o" % (w, r, nb)) for w, r, nb in MFMA_SHAPES]
 SOURCES = sorted(set(u[0] for u in UNITS))
 HEADERS = [os.path.join(CSRC, n) for n in ("tsw_internal.h", "tsw_device.h", "tsw_mfma_impl.h")] + [
     os.path.join(INCLUDE, "tsw.h")]

@@ -14,9 +14,10 @@
 // the full KV cache) and 无损的输出质量 (draft pass = same model over a
 // partial KV cache).
 //
-// Layout of the work: four wavefronts, one per SIMD, each owning NB or NB-1
-// blocks of 16 query rows (R row groups) and one 32-key sub-tile of every key
-// tile (4/R sub-tiles per tile).  Per tile:
+// Layout of the work: four wavefronts (one per SIMD, up to 512 registers) or
+// eight (two per SIMD, 256 registers), each owning NB or NB-1 blocks of 16
+// query rows (R row groups) and one 32-key sub-tile of every key tile
+// (W/R sub-tiles per tile).  Per tile:
 //   * K and V rows move HBM -> LDS with global_load_lds_dwordx4 into a
 //     128 KB ring (2, 4 or 8 stages); explicit s_waitcnt vmcnt keeps later
 //     tiles in flight, and one work-group barrier per tile recycles stages.
@@ -49,11 +50,11 @@ namespace mfma {
 // (logits far below zero) and precision could suffer; rerun exactly.
 constexpr float kMinRowSum = 0x1p-60f;
 
-template <int R_, int NB_>
+template <int W_, int R_, int NB_>
 struct Shape {
     static constexpr int R = R_;
     static constexpr int NB = NB_;
-    static constexpr int WAVES = 4;
+    static constexpr int WAVES = W_;
     static constexpr int KS = WAVES / R;            // 32-key sub-tiles per tile
     static constexpr int TK = 32 * KS;              // keys per tile
     static constexpr int ROWB = 256;                // bytes per K or V row
@@ -264,6 +265,52 @@ __device__ __forceinline__ void tile_pv(const SplitArgs& a, const Ctx& cx, int t
     }
 }
 
+// The same tile for waves that share their SIMD with a second wave (256
+// registers each): Q K for all blocks one head-dim step at a time, the
+// exponentials of all blocks, then P V one V column block at a time, so only
+// a step's K operands and one V operand are live.  The other wave on the
+// SIMD fills the matrix pipe while this one exponentiates.
+template <class S, int NBA, bool MASKED, bool SHIFT>
+__device__ __forceinline__ void tile_pv_shared(const SplitArgs& a, const Ctx& cx, int tt, float c, const char* Ks,
+                                               const char* Vs, const bf16x8 (&qop)[NBA][4], const float (&m)[NBA],
+                                               float (&l)[NBA], f32x4 (&o)[NBA][8]) {
+    f32x4 sc[NBA][2];
+#pragma unroll
+    for (int b = 0; b < NBA; ++b) s_init<S, MASKED>(a, cx, tt, b, sc[b]);
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+        const int row = cx.ks * 32 + kb * 16 + cx.li;
+        const char* base = Ks + row * S::ROWB;
+        const int sw = swz(row);
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            const bf16x8 kop = *(const bf16x8*)(base + 16 * ((4 * s + cx.lj) ^ sw));
+#pragma unroll
+            for (int b = 0; b < NBA; ++b)
+                sc[b][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qop[b][s], sc[b][kb], 0, 0, 0);
+        }
+    }
+    bf16x8 pb[NBA];
+#pragma unroll
+    for (int b = 0; b < NBA; ++b)
+        softmax_block<SHIFT>(sc[b], c, (SHIFT && m[b] != -INFINITY) ? m[b] : 0.0f, l[b], pb[b]);
+    const int trow0 = cx.ks * 32 + 4 * cx.lj + (cx.li >> 2);
+    const int trow1 = trow0 + 16;
+    const int tsel = (cx.li >> 1) & 1;
+    const char* vrow0 = Vs + trow0 * S::ROWB + 8 * (cx.li & 1);
+    const char* vrow1 = Vs + trow1 * S::ROWB + 8 * (cx.li & 1);
+    const int sw0 = swz(trow0) ^ tsel;
+    const int sw1 = swz(trow1) ^ tsel;
+#pragma unroll
+    for (int db = 0; db < 8; ++db) {
+        const bf16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vrow0 + 16 * ((2 * db) ^ sw0)));
+        const bf16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vrow1 + 16 * ((2 * db) ^ sw1)));
+        const bf16x8 vop = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+#pragma unroll
+        for (int b = 0; b < NBA; ++b) o[b][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pb[b], vop, o[b][db], 0, 0, 0);
+    }
+}
+
 // Row maxima of one tile (log2 units), folded into m: exact pass only.
 template <class S, int NBA, bool MASKED>
 __device__ __forceinline__ void tile_max(const SplitArgs& a, const Ctx& cx, int tt, float c, const bf16x8 (&kop)[2][4],
@@ -345,10 +392,14 @@ __device__ __forceinline__ void run_wave(const SplitArgs& a, const Ctx& cx) {
             // The stage of tile t-1 is free once every wave passed the barrier.
             if (t + STAGES - 1 < n) issue_tile<S, GATHER>(a, cx, t + STAGES - 1, (t + STAGES - 1) % STAGES);
             const char* Ks = cx.smem + (t % STAGES) * S::STAGE;
-            load_k<S>(Ks, cx, kop);
             if constexpr (MODE == MAXONLY) {
+                load_k<S>(Ks, cx, kop);
                 tile_max<S, NBA, MASKED>(a, cx, t, c, kop, qop, m_run);
+            } else if constexpr (S::WAVES == 8) {
+                tile_pv_shared<S, NBA, MASKED, MODE == EXACT>(a, cx, t, c, Ks, Ks + S::TK * S::ROWB, qop, m_run,
+                                                              l_run, o);
             } else {
+                load_k<S>(Ks, cx, kop);
                 load_v<S>(Ks + S::TK * S::ROWB, cx, vop);
                 tile_pv<S, NBA, MASKED, MODE == EXACT>(a, cx, t, c, kop, vop, qop, m_run, l_run, o);
             }
@@ -365,7 +416,7 @@ __device__ __forceinline__ void run_wave(const SplitArgs& a, const Ctx& cx) {
     // with any tile gives every row at least one visible key), and the
     // accumulators are finite.  Row sums are pooled through LDS first: one
     // wave's share of a row may legitimately hold no visible key.
-    float* pool = (float*)(cx.smem + S::smem(GATHER));      // [4 waves][NB][16]
+    float* pool = (float*)(cx.smem + S::smem(GATHER));      // [waves][NB][16]
     int* votes = (int*)(pool + S::WAVES * S::NB * 16);
     bool bad = false;
     float lq[NBA];
@@ -396,7 +447,10 @@ __device__ __forceinline__ void run_wave(const SplitArgs& a, const Ctx& cx) {
     // path, which keeps the barrier sequence identical across waves.
     if (cx.lane == 0) votes[cx.w] = __builtin_amdgcn_ballot_w64(bad) != 0;
     barrier_lds();
-    if (votes[0] | votes[1] | votes[2] | votes[3]) {
+    int any_vote = 0;
+#pragma unroll
+    for (int v = 0; v < S::WAVES; ++v) any_vote |= votes[v];
+    if (any_vote) {
 #pragma unroll
         for (int b = 0; b < NBA; ++b) m_run[b] = -INFINITY;
         pass(std::integral_constant<int, MAXONLY>{});
@@ -485,14 +539,15 @@ __device__ __forceinline__ void run_wave(const SplitArgs& a, const Ctx& cx) {
     }
 }
 
-template <int R, int NB, bool GATHER>
-__global__ __launch_bounds__(256, 1) void split_mfma(const SplitArgs a) {
-    using S = Shape<R, NB>;
+template <int W, int R, int NB, bool GATHER>
+__global__ __launch_bounds__(W * 64, 1) void split_mfma(const SplitArgs a) {
+    using S = Shape<W, R, NB>;
     constexpr int SMEM = S::smem(GATHER);
-    static_assert(SMEM + S::WAVES * NB * 16 * 4 + 16 <= 160 * 1024, "LDS budget");
+    constexpr int POOL = S::WAVES * NB * 16 * 4 + S::WAVES * 4;
+    static_assert(SMEM + POOL <= 160 * 1024, "LDS budget");
     static_assert(S::NI >= 1 && (S::TK / 2) % S::WAVES == 0, "tile / wave split");
     // + row-sum pool and votes used once after the fast pass
-    __shared__ __attribute__((aligned(1024))) char smem[SMEM + S::WAVES * NB * 16 * 4 + 16];
+    __shared__ __attribute__((aligned(1024))) char smem[SMEM + POOL];
 
     Ctx cx;
     cx.smem = smem;
@@ -532,11 +587,11 @@ __global__ __launch_bounds__(256, 1) void split_mfma(const SplitArgs a) {
     }
 }
 
-template <int R, int NB>
+template <int W, int R, int NB>
 hipError_t launch(bool gather, const SplitArgs& a, int n_kv_heads, hipStream_t stream) {
     const dim3 grid(a.n_splits, n_kv_heads);
-    if (gather) hipLaunchKernelGGL((split_mfma<R, NB, true>), grid, dim3(256), 0, stream, a);
-    else hipLaunchKernelGGL((split_mfma<R, NB, false>), grid, dim3(256), 0, stream, a);
+    if (gather) hipLaunchKernelGGL((split_mfma<W, R, NB, true>), grid, dim3(W * 64), 0, stream, a);
+    else hipLaunchKernelGGL((split_mfma<W, R, NB, false>), grid, dim3(W * 64), 0, stream, a);
     return hipGetLastError();
 }
 
