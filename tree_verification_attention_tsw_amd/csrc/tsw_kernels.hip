@@ -27,6 +27,8 @@
 //  * split_valu: float32 or bfloat16 inputs, d = 64 or 128, any row count;
 //    plain FMA dot products in fp32.  Exact fp32 path for float32 inputs and
 //    the fallback for shapes the matrix-core kernel does not cover.
+#include <type_traits>
+
 #include "tsw_device.h"
 #include "tsw_internal.h"
 
@@ -161,59 +163,80 @@ __global__ __launch_bounds__(256) void split_valu(const SplitArgs a) {
 // ---------------------------------------------------------------------------
 // One wavefront per output row: lanes hold the split LSEs (64 at a time),
 // wave reductions give the row's LSE, and each lane accumulates d/64
-// consecutive columns over the splits with coalesced loads.
+// consecutive columns over the splits with coalesced loads.  The partial
+// rows do not depend on the LSEs, so the first kMergeChunk of them are
+// loaded together with the LSEs: a row costs about one memory round trip.
+constexpr int kMergeChunk = 16;
+
 template <int D>
 __global__ __launch_bounds__(256) void lse_merge(int n_splits, int64_t n_rows,
                                                  const float* __restrict__ part_o,
                                                  const float* __restrict__ part_lse,
                                                  float* __restrict__ o, float* __restrict__ lse) {
     constexpr int PER = D / 64;
-    constexpr float kLog2e = 1.44269504088896340736f;
+    constexpr int CH = kMergeChunk;
+    using VT = typename std::conditional<PER == 2, float2, float>::type;
+    constexpr float kL2e = 1.44269504088896340736f;
     const int lane = threadIdx.x & 63;
     const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     if (r >= n_rows) return;
-    float mx = -INFINITY;
-    for (int s0 = 0; s0 < n_splits; s0 += 64)
+    const VT* src = (const VT*)(part_o + r * D) + lane;
+    const int64_t sstride = n_rows * D / PER;      // VT elements between splits
+
+    // chunk 0 of the partial rows (splits past the end re-read the last one
+    // and get weight 0), issued with the first 64 LSEs
+    VT x[CH];
+#pragma unroll
+    for (int j = 0; j < CH; ++j) x[j] = src[(int64_t)(j < n_splits ? j : n_splits - 1) * sstride];
+    const float ls0 = lane < n_splits ? part_lse[(int64_t)lane * n_rows + r] : -INFINITY;
+
+    float mx = ls0;
+    for (int s0 = 64; s0 < n_splits; s0 += 64)
         if (s0 + lane < n_splits) mx = fmaxf(mx, part_lse[(int64_t)(s0 + lane) * n_rows + r]);
 #pragma unroll
     for (int m = 32; m >= 1; m >>= 1) mx = xor_max(mx, m);
-    float acc[PER];
-#pragma unroll
-    for (int e = 0; e < PER; ++e) acc[e] = 0.0f;
     if (mx == -INFINITY) {
 #pragma unroll
         for (int e = 0; e < PER; ++e) o[r * D + lane * PER + e] = 0.0f;
         if (lane == 0) lse[r] = -INFINITY;
         return;
     }
-    float sum = 0.0f;
-    for (int s0 = 0; s0 < n_splits; s0 += 64)
+    float sum = ls0 == -INFINITY ? 0.0f : exp2f((ls0 - mx) * kL2e);
+    for (int s0 = 64; s0 < n_splits; s0 += 64)
         if (s0 + lane < n_splits) {
             const float ls = part_lse[(int64_t)(s0 + lane) * n_rows + r];
-            sum += ls == -INFINITY ? 0.0f : exp2f((ls - mx) * kLog2e);
+            sum += ls == -INFINITY ? 0.0f : exp2f((ls - mx) * kL2e);
         }
 #pragma unroll
     for (int m = 32; m >= 1; m >>= 1) sum = xor_sum(sum, m);
     const float L = mx + logf(sum);
-    for (int s0 = 0; s0 < n_splits; s0 += 64) {
-        float wl = 0.0f;
-        if (s0 + lane < n_splits) {
-            const float ls = part_lse[(int64_t)(s0 + lane) * n_rows + r];
-            wl = ls == -INFINITY ? 0.0f : exp2f((ls - L) * kLog2e);
-        }
-        const int n = n_splits - s0 < 64 ? n_splits - s0 : 64;
-#pragma unroll 8
-        for (int j = 0; j < n; ++j) {
-            const float wj = __shfl(wl, j);
-            const float* src = part_o + ((int64_t)(s0 + j) * n_rows + r) * D + lane * PER;
-            if constexpr (PER == 2) {
-                const float2 x = *(const float2*)src;
-                acc[0] = fmaf(wj, x.x, acc[0]);
-                acc[1] = fmaf(wj, x.y, acc[1]);
-            } else {
+
+    float acc[PER];
 #pragma unroll
-                for (int e = 0; e < PER; ++e) acc[e] = fmaf(wj, src[e], acc[e]);
+    for (int e = 0; e < PER; ++e) acc[e] = 0.0f;
+    auto fma_row = [&](float wj, const VT& v) {
+        if constexpr (PER == 2) {
+            acc[0] = fmaf(wj, v.x, acc[0]);
+            acc[1] = fmaf(wj, v.y, acc[1]);
+        } else {
+            acc[0] = fmaf(wj, v, acc[0]);
+        }
+    };
+    for (int s0 = 0; s0 < n_splits; s0 += 64) {
+        // weight of split s0 + lane (0 past the end)
+        const float ls = s0 == 0 ? ls0 : (s0 + lane < n_splits ? part_lse[(int64_t)(s0 + lane) * n_rows + r] : -INFINITY);
+        const float wl = ls == -INFINITY ? 0.0f : exp2f((ls - L) * kL2e);
+        const int ng = n_splits - s0 < 64 ? n_splits - s0 : 64;
+        for (int c0 = 0; c0 < ng; c0 += CH) {
+            if (s0 + c0 > 0) {
+#pragma unroll
+                for (int j = 0; j < CH; ++j) {
+                    const int sp = s0 + c0 + j < n_splits ? s0 + c0 + j : n_splits - 1;
+                    x[j] = src[(int64_t)sp * sstride];
+                }
             }
+#pragma unroll
+            for (int j = 0; j < CH; ++j) fma_row(__shfl(wl, c0 + j), x[j]);
         }
     }
 #pragma unroll

@@ -332,10 +332,17 @@ __device__ __forceinline__ void run_wave(const SplitArgs& a, const Ctx& cx) {
     constexpr int STAGES = S::STAGES;
     const float c = a.scale_log2;
 
+    const int n = cx.n_tiles;
+    // The first tiles of the fast pass go out before the Q loads, so the two
+    // latencies overlap; one drain then covers both and the tile loop never
+    // waits on Q.
+#pragma unroll
+    for (int s = 0; s < STAGES - 1; ++s)
+        if (s < n) issue_tile<S, GATHER>(a, cx, s, s);
+
     // Q^T as the B operand: lane (li, lj) holds query row li of the block,
     // head-dim elements 32*s + 8*lj .. +7.  Rows past M load row 0 and are
-    // zeroed.  The loads drain before the K/V pipeline starts, so the tile
-    // loop never waits on them.
+    // zeroed.
     bf16x8 qop[NBA][4];
 #pragma unroll
     for (int b = 0; b < NBA; ++b) {
@@ -364,21 +371,23 @@ __device__ __forceinline__ void run_wave(const SplitArgs& a, const Ctx& cx) {
 #pragma unroll
         for (int db = 0; db < 8; ++db) o[b][db] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
-    const int n = cx.n_tiles;
     bf16x8 kop[2][4], vop[8];
 
     // One pass over the split's tiles; every pass crosses one barrier per
-    // tile (plus one at its start), identically in all waves.
+    // tile (plus one at the start of a rerun), identically in all waves.
     //   FAST: p = 2^(s*c);  MAXONLY: exact row maxima;  EXACT: p = 2^(s*c - m).
+    // The fast pass's first tiles are already in flight.
     constexpr int FAST = 0, MAXONLY = 1, EXACT = 2;
     auto pass = [&](auto mode_c) {
         constexpr int MODE = decltype(mode_c)::value;
-        // no wave may refill the ring while another still reads the
-        // previous pass's last tile
-        barrier_lds();
+        if constexpr (MODE != FAST) {
+            // no wave may refill the ring while another still reads the
+            // previous pass's last tile
+            barrier_lds();
 #pragma unroll
-        for (int s = 0; s < STAGES - 1; ++s)
-            if (s < n) issue_tile<S, GATHER>(a, cx, s, s);
+            for (int s = 0; s < STAGES - 1; ++s)
+                if (s < n) issue_tile<S, GATHER>(a, cx, s, s);
+        }
         // Full prefix tiles come first; the ragged end of the slice and the
         // tree's own rows (masked) come last, so the two kinds run in two
         // consecutive loops with one copy of the tile code each.
@@ -467,45 +476,46 @@ __device__ __forceinline__ void run_wave(const SplitArgs& a, const Ctx& cx) {
 #pragma unroll
     for (int b = 0; b < NBA; ++b) l_run[b] = quad_sum(l_run[b]);
 
-    // Combine the KS key sub-tiles of each row group through LDS: waves with
-    // ks > 0 park their accumulators (lane-major, one f32x4 per lane) and
-    // their per-row (m, l); the ks = 0 wave merges and writes the partial.
+    // Combine the KS key sub-tiles of each row group through LDS.  Block b
+    // of a row group is finished by the wave with ks == b % KS; the other
+    // KS-1 waves park their accumulators for it (lane-major, one f32x4 per
+    // lane) with their per-row (m, l), in slot j = (ks - owner - 1) mod KS.
     f32x4* xo = (f32x4*)cx.smem;
     float* xml = (float*)(cx.smem + S::XSLOTS * 8 * 64 * 16);
+    auto slot = [&](int j, int b) { return (j * S::R + cx.rg) * S::NB + b; };
     if constexpr (S::KS > 1) {
         barrier_lds();
-        if (cx.ks > 0) {
 #pragma unroll
-            for (int b = 0; b < NBA; ++b) {
-                const int slot = ((cx.ks - 1) * S::R + cx.rg) * S::NB + b;
+        for (int b = 0; b < NBA; ++b) {
+            const int own = b % S::KS;
+            if (own == cx.ks) continue;
+            const int sl = slot((cx.ks - own - 1 + S::KS) % S::KS, b);
 #pragma unroll
-                for (int db = 0; db < 8; ++db) xo[(slot * 8 + db) * 64 + cx.lane] = o[b][db];
-                if (cx.lj == 0) {
-                    xml[slot * 32 + cx.li] = m_run[b];
-                    xml[slot * 32 + 16 + cx.li] = l_run[b];
-                }
+            for (int db = 0; db < 8; ++db) xo[(sl * 8 + db) * 64 + cx.lane] = o[b][db];
+            if (cx.lj == 0) {
+                xml[sl * 32 + cx.li] = m_run[b];
+                xml[sl * 32 + 16 + cx.li] = l_run[b];
             }
         }
         barrier_lds();
-        if (cx.ks > 0) return;
     }
 
 #pragma unroll
     for (int b = 0; b < NBA; ++b) {
-        // per-row weights, computed by the lanes that own row li
-        float wk[S::KS];
+        if (b % S::KS != cx.ks) continue;
+        // per-row weights of the KS partial sums, computed by the lanes that
+        // own row li (own sums first, then the parked ones)
         float mmax = m_run[b];
 #pragma unroll
-        for (int k2 = 1; k2 < S::KS; ++k2)
-            mmax = fmaxf(mmax, xml[(((k2 - 1) * S::R + cx.rg) * S::NB + b) * 32 + cx.li]);
-        float L = 0.0f;
+        for (int j = 0; j < S::KS - 1; ++j) mmax = fmaxf(mmax, xml[slot(j, b) * 32 + cx.li]);
+        const float w0 = m_run[b] == -INFINITY ? 0.0f : exp2_fast(m_run[b] - mmax);
+        float L = w0 * l_run[b];
+        float wk[S::KS > 1 ? S::KS - 1 : 1];
 #pragma unroll
-        for (int k2 = 0; k2 < S::KS; ++k2) {
-            const int slot = ((k2 - 1) * S::R + cx.rg) * S::NB + b;
-            const float mk = k2 == 0 ? m_run[b] : xml[slot * 32 + cx.li];
-            const float lk = k2 == 0 ? l_run[b] : xml[slot * 32 + 16 + cx.li];
-            wk[k2] = mk == -INFINITY ? 0.0f : exp2_fast(mk - mmax);
-            L += wk[k2] * lk;
+        for (int j = 0; j < S::KS - 1; ++j) {
+            const float mk = xml[slot(j, b) * 32 + cx.li];
+            wk[j] = mk == -INFINITY ? 0.0f : exp2_fast(mk - mmax);
+            L += wk[j] * xml[slot(j, b) * 32 + 16 + cx.li];
         }
         const float inv = L > 0.0f ? 1.0f / L : 0.0f;
         const int rbase = (cx.rg + b * S::R) * 16;
@@ -518,21 +528,19 @@ __device__ __forceinline__ void run_wave(const SplitArgs& a, const Ctx& cx) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int q = 4 * cx.lj + i;
-            float wq[S::KS];
+            const float wq0 = __shfl(w0 * inv, q);
+            float wq[S::KS > 1 ? S::KS - 1 : 1];
 #pragma unroll
-            for (int k2 = 0; k2 < S::KS; ++k2) wq[k2] = __shfl(wk[k2] * inv, q);
+            for (int j = 0; j < S::KS - 1; ++j) wq[j] = __shfl(wk[j] * inv, q);
             const int r = rbase + q;
             if (r >= a.M) continue;
             const size_t orow = ((size_t)cx.split * a.T + r / a.G) * a.Hq + cx.g * a.G + r % a.G;
             float* dst = a.part_o + orow * 128 + cx.li;
 #pragma unroll
             for (int db = 0; db < 8; ++db) {
-                float acc = o[b][db][i] * wq[0];
+                float acc = o[b][db][i] * wq0;
 #pragma unroll
-                for (int k2 = 1; k2 < S::KS; ++k2) {
-                    const int slot = ((k2 - 1) * S::R + cx.rg) * S::NB + b;
-                    acc += wq[k2] * xo[(slot * 8 + db) * 64 + cx.lane][i];
-                }
+                for (int j = 0; j < S::KS - 1; ++j) acc += wq[j] * xo[(slot(j, b) * 8 + db) * 64 + cx.lane][i];
                 dst[16 * db] = acc;
             }
         }
