@@ -374,3 +374,48 @@ def test_large_logit_headroom(where):
     if where != "tree_row":
         assert float(np.min(l_ref[:, 0])) - float(np.median(l_ref)) > 45.0
     check(o, lse, o_ref, l_ref, TOL["bf16"], "large logit %s" % where)
+
+
+def test_hip_graph_replays_match_eager():
+    """Verify and partial calls captured in one HIP graph: every replay, with
+    eager work and synchronisations in between, equals the eager result bit
+    for bit (the library records only kernel launches)."""
+    T, Hq, Hkv, d, npre = 40, 32, 8, 128, 6000
+    parent = wl.kary_tree_parent(T, 3)
+    q = gen((T, Hq, d), 91, torch.bfloat16)
+    k = gen((Hkv, npre + T, d), 92, torch.bfloat16)
+    v = gen((Hkv, npre + T, d), 93, torch.bfloat16)
+    qp = gen((4, Hq, d), 94, torch.bfloat16)
+    kp = gen((Hkv, npre + 4, d), 95, torch.bfloat16)
+    vp = gen((Hkv, npre + 4, d), 96, torch.bfloat16)
+    chain = wl.chain_parent(4)
+    idx = torch.from_numpy(np.sort(np.random.default_rng(9).choice(npre, 1500, replace=False))
+                           .astype(np.int32)).cuda()
+    o_e, l_e = tsw.tree_attn_verify(q, k, v, parent, npre)
+    op_e, lp_e = tsw.tree_attn_partial(qp, kp, vp, chain, idx, npre)
+    torch.cuda.synchronize()
+
+    cs = torch.cuda.Stream()
+    o = torch.empty_like(o_e); lse = torch.empty_like(l_e)
+    op = torch.empty_like(op_e); lp = torch.empty_like(lp_e)
+    ws = torch.empty(max(tsw.workspace_size(q, k, npre), 256), dtype=torch.uint8, device=q.device)
+    wsp = torch.empty(max(tsw.workspace_size(qp, kp, npre, idx.numel()), 256), dtype=torch.uint8,
+                      device=q.device)
+    c1 = tsw.prepare_verify(q, k, v, parent, npre, o, lse, ws, stream=cs)
+    c2 = tsw.prepare_verify(qp, kp, vp, chain, npre, op, lp, wsp, idx=idx, stream=cs)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=cs):
+        c1()
+        c2()
+    for rep in range(4):
+        for t in (o, lse, op, lp):
+            t.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        # eager work between replays reuses the same kernels
+        tsw.tree_attn_verify(q, k, v, parent, npre)
+        torch.cuda.synchronize()
+        assert torch.equal(o, o_e) and torch.equal(lse, l_e), rep
+        assert torch.equal(op, op_e) and torch.equal(lp, lp_e), rep
+    say("graph replays: 4 x bit-identical")

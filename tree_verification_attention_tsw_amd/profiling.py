@@ -1,0 +1,173 @@
+"""Text summaries of rocprofv3 output for this library's kernels.
+
+Two kinds of summary, both short text files meant to be kept beside the
+numbers they support:
+
+* kernel timing: ``rocprofv3 --kernel-trace --stats`` output reduced to the
+  calls, average, minimum and maximum duration of every ``tsw::`` kernel;
+* HBM traffic: two ``rocprofv3 --pmc`` runs (``FETCH_SIZE``, then
+  ``WRITE_SIZE``, KiB per dispatch) reduced to bytes per launch of one
+  kernel, each counter scaled by what it reads for a plain float32
+  elementwise copy of known size run in the same process (bench.py
+  ``--copy-calibration-mib``).
+
+The traffic summary records a digest of the kernel sources so that a reader
+(bench.py) can tell whether the counters still describe the current code.
+
+    python -m tree_verification_attention_tsw_amd.profiling stats DIR OUT --command "..."
+    python -m tree_verification_attention_tsw_amd.profiling traffic FETCH_DIR WRITE_DIR OUT \\
+        --kernel split_mfma --copy-mib 1024 --alg-bytes N --command "..." --command "..."
+"""
+import argparse
+import collections
+import csv
+import glob
+import hashlib
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+COPY_KERNEL_MARK = "MulFunctor<float>"
+
+
+def source_digest():
+    """sha256 over the kernel and C-ABI sources (name + bytes, sorted)."""
+    h = hashlib.sha256()
+    files = sorted(glob.glob(os.path.join(PKG, "csrc", "*")) + glob.glob(os.path.join(ROOT, "include", "*.h")))
+    for f in files:
+        h.update(os.path.relpath(f, ROOT).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def _find(d, suffix):
+    hits = sorted(glob.glob(os.path.join(d, "**", "*" + suffix), recursive=True))
+    if not hits:
+        raise FileNotFoundError("no *%s under %s" % (suffix, d))
+    return hits[-1]
+
+
+def _short(name):
+    """'void tsw::mfma::split_mfma<8, 4, 3, false>(tsw::SplitArgs)' -> 'split_mfma<8, 4, 3, false>'."""
+    n = name.replace("(anonymous namespace)::", "").split("(")[0]
+    if n.startswith("void "):
+        n = n[5:]
+    return n.split("::")[-1] if "tsw::" in n else n[:60]
+
+
+def kernel_stats(d):
+    rows = list(csv.DictReader(open(_find(d, "_kernel_stats.csv"))))
+    out = []
+    for r in rows:
+        if "tsw::" not in r["Name"]:
+            continue
+        out.append((_short(r["Name"]), int(r["Calls"]), float(r["AverageNs"]) / 1e3,
+                    float(r["MinNs"]) / 1e3, float(r["MaxNs"]) / 1e3))
+    return out
+
+
+def counter_rows(d):
+    return list(csv.DictReader(open(_find(d, "_counter_collection.csv"))))
+
+
+def per_dispatch(rows, counter, kernel_substr):
+    """Counter values of every dispatch whose name contains kernel_substr."""
+    vals = collections.OrderedDict()
+    for r in rows:
+        if r["Counter_Name"] != counter or kernel_substr not in r["Kernel_Name"]:
+            continue
+        key = int(r["Dispatch_Id"])
+        vals[key] = vals.get(key, 0.0) + float(r["Counter_Value"])
+    return list(vals.values())
+
+
+def copy_factor(rows, counter, copy_bytes):
+    """Bytes per counted KiB, from the calibration copy (largest such dispatch)."""
+    v = per_dispatch(rows, counter, COPY_KERNEL_MARK)
+    if not v:
+        raise ValueError("no calibration copy dispatch (%s) in the %s run" % (COPY_KERNEL_MARK, counter))
+    kib = max(v)
+    return copy_bytes / (kib * 1024.0), kib
+
+
+def write_stats(d, out, commands):
+    lines = ["# rocprofv3 kernel durations of the tsw kernels", "commands:"]
+    lines += ["  " + c for c in commands]
+    lines.append("source_digest: %s" % source_digest())
+    lines.append("%-44s %6s %10s %10s %10s" % ("kernel", "calls", "avg_us", "min_us", "max_us"))
+    for name, calls, avg, mn, mx in kernel_stats(d):
+        lines.append("%-44s %6d %10.2f %10.2f %10.2f" % (name, calls, avg, mn, mx))
+    _write(out, lines)
+
+
+def write_traffic(fetch_dir, write_dir, out, kernel, copy_mib, alg_bytes, commands):
+    copy_bytes = copy_mib * 2 ** 20
+    fr, wr = counter_rows(fetch_dir), counter_rows(write_dir)
+    ff, fkib = copy_factor(fr, "FETCH_SIZE", copy_bytes)
+    wf, wkib = copy_factor(wr, "WRITE_SIZE", copy_bytes)
+    fv = per_dispatch(fr, "FETCH_SIZE", kernel)
+    wv = per_dispatch(wr, "WRITE_SIZE", kernel)
+    if not fv or not wv:
+        raise ValueError("no %s dispatches in the counter runs" % kernel)
+    fb = sum(fv) / len(fv) * 1024.0 * ff
+    wb = sum(wv) / len(wv) * 1024.0 * wf
+    lines = ["# HBM traffic per launch of %s (rocprofv3 --pmc, copy-calibrated)" % kernel, "commands:"]
+    lines += ["  " + c for c in commands]
+    lines.append("source_digest: %s" % source_digest())
+    lines.append("copy_calibration: %d bytes read and written; FETCH_SIZE %.1f KiB -> %.4f bytes/KiB-unit; "
+                 "WRITE_SIZE %.1f KiB -> %.4f" % (copy_bytes, fkib, ff * 1024, wkib, wf * 1024))
+    lines.append("dispatches: fetch run %d, write run %d" % (len(fv), len(wv)))
+    lines.append("fetch_bytes_per_launch: %.0f" % fb)
+    lines.append("write_bytes_per_launch: %.0f" % wb)
+    lines.append("traffic_bytes_per_launch: %.0f" % (fb + wb))
+    if alg_bytes:
+        lines.append("alg_bytes_per_launch: %d" % alg_bytes)
+        lines.append("traffic_over_alg: %.4f" % ((fb + wb) / alg_bytes))
+    _write(out, lines)
+
+
+def read_traffic(path):
+    """(traffic bytes per launch, digest) from a traffic summary, or None."""
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if ":" in line and not line.startswith(" "):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    if "traffic_bytes_per_launch" not in kv or "source_digest" not in kv:
+        return None
+    return float(kv["traffic_bytes_per_launch"]), kv["source_digest"]
+
+
+def _write(out, lines):
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    s = sub.add_parser("stats")
+    s.add_argument("dir")
+    s.add_argument("out")
+    s.add_argument("--command", action="append", default=[])
+    t = sub.add_parser("traffic")
+    t.add_argument("fetch_dir")
+    t.add_argument("write_dir")
+    t.add_argument("out")
+    t.add_argument("--kernel", default="split_mfma")
+    t.add_argument("--copy-mib", type=int, required=True)
+    t.add_argument("--alg-bytes", type=int, default=0)
+    t.add_argument("--command", action="append", default=[])
+    a = ap.parse_args()
+    if a.cmd == "stats":
+        write_stats(a.dir, a.out, a.command)
+    else:
+        write_traffic(a.fetch_dir, a.write_dir, a.out, a.kernel, a.copy_mib, a.alg_bytes, a.command)
+
+
+if __name__ == "__main__":
+    main()
