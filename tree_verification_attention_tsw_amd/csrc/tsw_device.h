@@ -56,6 +56,24 @@ __device__ __forceinline__ void wait_vmcnt() {
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
+// Transposed 64-bit LDS read (ds_read_b64_tr_b16) issued through inline
+// assembly.  Through the builtin, the compiler puts s_waitcnt vmcnt(0) in
+// front of every such read while LDS-DMA loads are outstanding, which would
+// drain the whole K/V prefetch ring once per tile.  Here the compiler does not
+// see the read: the caller must call lds_wait() on the results before use.
+__device__ __forceinline__ bf16x4 ds_read_tr16_b64(const char* p) {
+    bf16x4 r;
+    const uint32_t a = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
+    asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(r) : "v"(a));
+    return r;
+}
+
+// Wait for every outstanding LDS read (and scalar load); tying the values
+// keeps their uses after the wait.
+__device__ __forceinline__ void lds_wait(bf16x4& x, bf16x4& y) {
+    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(x), "+v"(y));
+}
+
 // Work-group barrier that does not wait for outstanding LDS-DMA loads (the
 // pipelines wait for exactly the tiles they need with wait_vmcnt).  Pending
 // LDS reads are drained first so a stage is never overwritten under a read.

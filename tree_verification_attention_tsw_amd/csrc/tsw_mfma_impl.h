@@ -50,7 +50,7 @@ namespace mfma {
 // (logits far below zero) and precision could suffer; rerun exactly.
 constexpr float kMinRowSum = 0x1p-60f;
 
-template <int W_, int R_, int NB_>
+template <int W_, int R_, int NB_, bool GATHER_>
 struct Shape {
     static constexpr int R = R_;
     static constexpr int NB = NB_;
@@ -59,21 +59,30 @@ struct Shape {
     static constexpr int TK = 32 * KS;              // keys per tile
     static constexpr int ROWB = 256;                // bytes per K or V row
     static constexpr int STAGE = 2 * TK * ROWB;     // one K tile + one V tile
-    static constexpr int RING = 128 * 1024;
-    static constexpr int STAGES = RING / STAGE;     // 2, 4 or 8
     static constexpr int NI = TK / (2 * WAVES);     // DMA instructions per wave per tile
+    // LDS beyond the ring: row-sum pool and votes, the tree mask, and for
+    // the gather variant the staged index slice.
+    static constexpr int POOL = WAVES * NB * 16 * 4 + WAVES * 4;
+    static constexpr int MASK_BYTES = 64 * 8;
+    static constexpr int IDX_BYTES = GATHER_ ? kGatherChunkMax * 4 : 0;
+    static constexpr int RESERVE = ((POOL + MASK_BYTES + 255) & ~255) + IDX_BYTES;
+    // as many stages as the LDS holds (up to 16): more tiles in flight
+    static constexpr int STAGES_FIT = (160 * 1024 - RESERVE) / STAGE;
+    static constexpr int STAGES = STAGES_FIT < 16 ? STAGES_FIT : 16;
+    static constexpr int RING = STAGES * STAGE;
     static constexpr int XSLOTS = (KS - 1) * R * NB;   // parked (wave, block) pairs
     static constexpr int XBYTES = XSLOTS * (8 * 64 * 16 + 32 * 4);
-    static constexpr int IDX_BYTES = kGatherChunkMax * 4;
-    static constexpr int smem(bool gather) {
-        const int loop = RING + (gather ? IDX_BYTES : 0);
-        return loop > XBYTES ? loop : XBYTES;
-    }
+    // ring (+ index slice) during the loop, the KS exchange afterwards
+    static constexpr int LOOP_BYTES = RING + IDX_BYTES;
+    static constexpr int SMEM = LOOP_BYTES > XBYTES ? LOOP_BYTES : XBYTES;
+    static_assert(STAGES >= 2, "at least two ring stages");
+    static_assert((STAGES - 1) * NI < 64, "vmcnt range");
 };
 
 struct Ctx {
     char* smem;
     const int32_t* idx_lds;
+    const uint64_t* mask_lds;    // the tree mask, copied to LDS
     const char* kbase;
     const char* vbase;
     int64_t c0, c1;      // prefix key range [c0, c1) of this split
@@ -131,22 +140,18 @@ __device__ __forceinline__ void issue_tile(const SplitArgs& a, const Ctx& cx, in
 }
 
 // Wait until this wave's loads of the oldest pending tile have landed while
-// `newer` later tiles stay in flight.
-template <class S>
+// `newer` later tiles stay in flight (0 <= newer <= K).
+template <class S, int K = S::STAGES - 2>
 __device__ __forceinline__ void wait_tile(int newer) {
-    if constexpr (S::STAGES >= 8) {
-        if (newer >= 6) { wait_vmcnt<6 * S::NI>(); return; }
-        if (newer == 5) { wait_vmcnt<5 * S::NI>(); return; }
-        if (newer == 4) { wait_vmcnt<4 * S::NI>(); return; }
-        if (newer == 3) { wait_vmcnt<3 * S::NI>(); return; }
+    if constexpr (K <= 0) {
+        wait_vmcnt<0>();
+    } else {
+        if (newer >= K) {
+            wait_vmcnt<K * S::NI>();
+            return;
+        }
+        wait_tile<S, K - 1>(newer);
     }
-    if constexpr (S::STAGES >= 4) {
-        if (newer >= 2) { wait_vmcnt<2 * S::NI>(); return; }
-    }
-    if constexpr (S::STAGES >= 3) {
-        if (newer >= 1) { wait_vmcnt<S::NI>(); return; }
-    }
-    wait_vmcnt<0>();
 }
 
 // K operands of this wave's 32-key sub-tile: lane (li, lj) holds key row
@@ -174,11 +179,16 @@ __device__ __forceinline__ void load_v(const char* Vs, const Ctx& cx, bf16x8 (&v
     const char* vrow1 = Vs + trow1 * S::ROWB + 8 * (cx.li & 1);
     const int sw0 = swz(trow0) ^ tsel;
     const int sw1 = swz(trow1) ^ tsel;
+    bf16x4 v0[8], v1[8];
 #pragma unroll
     for (int db = 0; db < 8; ++db) {
-        const bf16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vrow0 + 16 * ((2 * db) ^ sw0)));
-        const bf16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vrow1 + 16 * ((2 * db) ^ sw1)));
-        vop[db] = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+        v0[db] = ds_read_tr16_b64(vrow0 + 16 * ((2 * db) ^ sw0));
+        v1[db] = ds_read_tr16_b64(vrow1 + 16 * ((2 * db) ^ sw1));
+    }
+#pragma unroll
+    for (int db = 0; db < 8; ++db) {
+        lds_wait(v0[db], v1[db]);
+        vop[db] = __builtin_shufflevector(v0[db], v1[db], 0, 1, 2, 3, 4, 5, 6, 7);
     }
 }
 
@@ -197,7 +207,7 @@ __device__ __forceinline__ void s_init(const SplitArgs& a, const Ctx& cx, int tt
         const int64_t kstart = tail ? (int64_t)(tt - cx.n_pre_tiles) * S::TK : cx.c0 + (int64_t)tt * S::TK;
         const int64_t kend = tail ? a.T : cx.c1;
         const int r = (cx.rg + b * S::R) * 16 + cx.li;
-        const uint64_t nmask = (tail && r < a.M) ? a.mask[r / a.G] : ~0ull;
+        const uint64_t nmask = (tail && r < a.M) ? cx.mask_lds[r / a.G] : ~0ull;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -301,11 +311,18 @@ __device__ __forceinline__ void tile_pv_shared(const SplitArgs& a, const Ctx& cx
     const char* vrow1 = Vs + trow1 * S::ROWB + 8 * (cx.li & 1);
     const int sw0 = swz(trow0) ^ tsel;
     const int sw1 = swz(trow1) ^ tsel;
+    // V operands for column block db+1 are read while the products of block
+    // db run.
+    bf16x4 c0 = ds_read_tr16_b64(vrow0 + 16 * (0 ^ sw0));
+    bf16x4 c1 = ds_read_tr16_b64(vrow1 + 16 * (0 ^ sw1));
 #pragma unroll
     for (int db = 0; db < 8; ++db) {
-        const bf16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vrow0 + 16 * ((2 * db) ^ sw0)));
-        const bf16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vrow1 + 16 * ((2 * db) ^ sw1)));
-        const bf16x8 vop = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+        lds_wait(c0, c1);
+        const bf16x8 vop = __builtin_shufflevector(c0, c1, 0, 1, 2, 3, 4, 5, 6, 7);
+        if (db + 1 < 8) {
+            c0 = ds_read_tr16_b64(vrow0 + 16 * ((2 * (db + 1)) ^ sw0));
+            c1 = ds_read_tr16_b64(vrow1 + 16 * ((2 * (db + 1)) ^ sw1));
+        }
 #pragma unroll
         for (int b = 0; b < NBA; ++b) o[b][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pb[b], vop, o[b][db], 0, 0, 0);
     }
@@ -333,34 +350,33 @@ __device__ __forceinline__ void run_wave(const SplitArgs& a, const Ctx& cx) {
     const float c = a.scale_log2;
 
     const int n = cx.n_tiles;
-    // The first tiles of the fast pass go out before the Q loads, so the two
-    // latencies overlap; one drain then covers both and the tile loop never
-    // waits on Q.
-#pragma unroll
-    for (int s = 0; s < STAGES - 1; ++s)
-        if (s < n) issue_tile<S, GATHER>(a, cx, s, s);
-
     // Q^T as the B operand: lane (li, lj) holds query row li of the block,
-    // head-dim elements 32*s + 8*lj .. +7.  Rows past M load row 0 and are
-    // zeroed.
+    // head-dim elements 32*s + 8*lj .. +7.  Rows past M repeat the first row
+    // of this head group (their results are never stored).
     bf16x8 qop[NBA][4];
 #pragma unroll
     for (int b = 0; b < NBA; ++b) {
         const int r = (cx.rg + b * S::R) * 16 + cx.li;
         const bool ok = r < a.M;
         const int t = ok ? r / a.G : 0;
-        const int h = ok ? cx.g * a.G + r % a.G : 0;
+        const int h = cx.g * a.G + (ok ? r % a.G : 0);
         const bf16x8* src = (const bf16x8*)((const __bf16*)a.q + ((size_t)t * a.Hq + h) * 128 + 8 * cx.lj);
 #pragma unroll
         for (int s = 0; s < 4; ++s) qop[b][s] = src[4 * s];
-        if (!ok) {
-#pragma unroll
-            for (int s = 0; s < 4; ++s)
-#pragma unroll
-                for (int e = 0; e < 8; ++e) qop[b][s][e] = (__bf16)0.0f;
-        }
     }
-    wait_vmcnt<0>();
+    // The fast pass's first tiles go out right behind the Q loads; the wait
+    // below lets exactly those tile loads stay in flight, so the Q latency
+    // hides under the first tile's and the tile loop never waits on Q.
+    if (n >= STAGES - 1) {
+#pragma unroll
+        for (int s = 0; s < STAGES - 1; ++s) issue_tile<S, GATHER>(a, cx, s, s);
+        wait_vmcnt<(STAGES - 1) * S::NI>();
+    } else {
+#pragma unroll
+        for (int s = 0; s < STAGES - 1; ++s)
+            if (s < n) issue_tile<S, GATHER>(a, cx, s, s);
+        wait_vmcnt<0>();
+    }
 
     float m_run[NBA], l_run[NBA];
     f32x4 o[NBA][8];
@@ -425,7 +441,7 @@ __device__ __forceinline__ void run_wave(const SplitArgs& a, const Ctx& cx) {
     // with any tile gives every row at least one visible key), and the
     // accumulators are finite.  Row sums are pooled through LDS first: one
     // wave's share of a row may legitimately hold no visible key.
-    float* pool = (float*)(cx.smem + S::smem(GATHER));      // [waves][NB][16]
+    float* pool = (float*)(cx.smem + S::SMEM);      // [waves][NB][16]
     int* votes = (int*)(pool + S::WAVES * S::NB * 16);
     bool bad = false;
     float lq[NBA];
@@ -549,13 +565,16 @@ __device__ __forceinline__ void run_wave(const SplitArgs& a, const Ctx& cx) {
 
 template <int W, int R, int NB, bool GATHER>
 __global__ __launch_bounds__(W * 64, 1) void split_mfma(const SplitArgs a) {
-    using S = Shape<W, R, NB>;
-    constexpr int SMEM = S::smem(GATHER);
-    constexpr int POOL = S::WAVES * NB * 16 * 4 + S::WAVES * 4;
-    static_assert(SMEM + POOL <= 160 * 1024, "LDS budget");
+    using S = Shape<W, R, NB, GATHER>;
+    constexpr int SMEM = S::SMEM;
+    constexpr int MASK_OFF = (SMEM + S::POOL + 7) & ~7;
+    static_assert(MASK_OFF + 64 * 8 <= 160 * 1024, "LDS budget");
     static_assert(S::NI >= 1 && (S::TK / 2) % S::WAVES == 0, "tile / wave split");
-    // + row-sum pool and votes used once after the fast pass
-    __shared__ __attribute__((aligned(1024))) char smem[SMEM + POOL];
+    // + row-sum pool and votes used once after the fast pass, + the tree mask
+    // (read from LDS in masked tiles: a per-lane read of the kernel
+    // arguments would be a vector memory load, and waiting for it would
+    // drain the K/V ring)
+    __shared__ __attribute__((aligned(1024))) char smem[MASK_OFF + 64 * 8];
 
     Ctx cx;
     cx.smem = smem;
@@ -577,6 +596,10 @@ __global__ __launch_bounds__(W * 64, 1) void split_mfma(const SplitArgs a) {
     cx.vbase = (const char*)a.v + (size_t)cx.g * (size_t)a.kv_head_stride * 2;
     int32_t* idx_lds = (int32_t*)(smem + S::RING);
     cx.idx_lds = idx_lds;
+    uint64_t* mask_lds = (uint64_t*)(smem + MASK_OFF);
+    cx.mask_lds = mask_lds;
+    // visible to all waves after the first barrier of the tile loop
+    if (threadIdx.x < (unsigned)a.T) mask_lds[threadIdx.x] = a.mask[threadIdx.x];
     if constexpr (GATHER) {
         const int n = (int)(cx.c1 > cx.c0 ? cx.c1 - cx.c0 : 0);
         for (int i = threadIdx.x; i < n; i += S::WAVES * 64) idx_lds[i] = a.idx[cx.c0 + i];
