@@ -166,7 +166,7 @@ __global__ __launch_bounds__(256) void split_valu(const SplitArgs a) {
 // consecutive columns over the splits with coalesced loads.  The partial
 // rows do not depend on the LSEs, so the first kMergeChunk of them are
 // loaded together with the LSEs: a row costs about one memory round trip.
-constexpr int kMergeChunk = 16;
+constexpr int kMergeChunk = 32;
 
 template <int D>
 __global__ __launch_bounds__(256) void lse_merge(int n_splits, int64_t n_rows,
