@@ -540,25 +540,38 @@ __device__ __forceinline__ void run_wave(const SplitArgs& a, const Ctx& cx) {
             const size_t orow = ((size_t)cx.split * a.T + r / a.G) * a.Hq + cx.g * a.G + r % a.G;
             a.part_lse[orow] = L > 0.0f ? (mmax + __log2f(L)) * kLn2 : -INFINITY;
         }
-        // accumulator element i of this lane belongs to row 4*lj + i
+        // accumulator element i of this lane belongs to row 4*lj + i; the
+        // per-row weights and destinations are formed once, then each
+        // column block reads its parked partner sums together
+        float wq0[4], wq[4][S::KS > 1 ? S::KS - 1 : 1];
+        float* dst[4];
+        bool row_ok[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int q = 4 * cx.lj + i;
-            const float wq0 = __shfl(w0 * inv, q);
-            float wq[S::KS > 1 ? S::KS - 1 : 1];
+            wq0[i] = __shfl(w0 * inv, q);
 #pragma unroll
-            for (int j = 0; j < S::KS - 1; ++j) wq[j] = __shfl(wk[j] * inv, q);
+            for (int j = 0; j < S::KS - 1; ++j) wq[i][j] = __shfl(wk[j] * inv, q);
             const int r = rbase + q;
-            if (r >= a.M) continue;
-            const size_t orow = ((size_t)cx.split * a.T + r / a.G) * a.Hq + cx.g * a.G + r % a.G;
-            float* dst = a.part_o + orow * 128 + cx.li;
+            row_ok[i] = r < a.M;
+            const int rr = row_ok[i] ? r : rbase;
+            const size_t orow = ((size_t)cx.split * a.T + rr / a.G) * a.Hq + cx.g * a.G + rr % a.G;
+            dst[i] = a.part_o + orow * 128 + cx.li;
+        }
 #pragma unroll
-            for (int db = 0; db < 8; ++db) {
-                float acc = o[b][db][i] * wq0;
+        for (int db = 0; db < 8; ++db) {
+            float acc[4];
 #pragma unroll
-                for (int j = 0; j < S::KS - 1; ++j) acc += wq[j] * xo[(slot(j, b) * 8 + db) * 64 + cx.lane][i];
-                dst[16 * db] = acc;
+            for (int i = 0; i < 4; ++i) acc[i] = o[b][db][i] * wq0[i];
+#pragma unroll
+            for (int j = 0; j < S::KS - 1; ++j) {
+                const f32x4 x = xo[(slot(j, b) * 8 + db) * 64 + cx.lane];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) acc[i] += wq[i][j] * x[i];
             }
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                if (row_ok[i]) dst[i][16 * db] = acc[i];
         }
     }
 }
