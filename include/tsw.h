@@ -152,6 +152,59 @@ int tsw_lse_merge(int32_t n_splits, int64_t n_rows, int32_t d, const float* part
                   const float* part_lse, float* o, float* lse, tsw_stream_t stream);
 
 /* Static description of a status code. */
+/* ---------------------------------------------------------------------
+ * After verification: greedy acceptance and accepted-path KV compaction.
+ *
+ * The target model's logits at each tree node give its most likely next
+ * token there (first index among equal maxima).  Node i > 0 is accepted when
+ * its parent is accepted and draft[i] equals that token at parent[i]; the
+ * root (node 0, the committed token) is always accepted.  The output path is
+ * the root path of the deepest accepted node (lowest index among equally
+ * deep ones), and the bonus token is the target's most likely token after
+ * it.  Sources: "TokenSwift - A framework for accelerating the generation of
+ * ultra-long text" (aiboss88), technical principles, tree-based
+ * multi-candidate token verification (the longest valid candidate is kept;
+ * the output stays consistent with the target model); Tencent Cloud article
+ * "90分钟生成10万Token，新框架实现3倍无损加速超长文本生成", 技术原理
+ * (parallel-verification figure text: the longest valid sequence is kept).
+ * The pages pick randomly among equally long candidates or just "the
+ * longest"; this library takes the lowest node index, which never matters
+ * when sibling tokens are distinct.
+ * ------------------------------------------------------------------- */
+
+/* Workspace bytes tsw_accept_greedy needs for T nodes and this vocabulary
+ * on the current device.  TSW_EINVAL for T outside 1..64 or vocab outside
+ * 1..2^31-1. */
+int tsw_accept_workspace_size(int32_t T, int64_t vocab, size_t* bytes);
+
+/* logits [T][vocab] (device, float32 or bfloat16 per logits_dtype, rows
+ * contiguous), draft [T] int32 (device; draft[0] is not read), parent [T]
+ * int32 (HOST, same encoding as above).  Writes result (device, int32,
+ * 2 + 2*T entries): result[0] = L (path length, 1..T), result[1] = bonus
+ * token, result[2 .. 2+L) = the path's node indices from the root,
+ * result[2+L .. 2+T) = -1, result[2+T .. 2+2T) = the most likely token at
+ * every node.  workspace: device, >= tsw_accept_workspace_size() bytes,
+ * 8-byte aligned, scratch.  NaN logits are outside the contract (a row of
+ * NaN reports token 0).  Errors: TSW_EINVAL, TSW_EBADTREE, TSW_EUNSUPPORTED
+ * (dtype), TSW_ENOSPACE, TSW_EHIP. */
+int tsw_accept_greedy(const int32_t* parent, int32_t T, const void* logits, int64_t vocab,
+                      int32_t logits_dtype, const int32_t* draft, int32_t* result, void* workspace,
+                      size_t workspace_bytes, tsw_stream_t stream);
+
+/* Moves the accepted path's K and V rows into place for n_layers caches:
+ * for k = 1 .. L-1 the row at n_prefix + path[k] is copied to n_prefix + k
+ * (row n_prefix + 0, the root, stays); the caller then commits
+ * n_prefix + L positions.  k, v: device, layer l at element offset
+ * l * layer_stride, each [Hkv][rows][d] with kv_head_stride elements between
+ * heads, rows >= n_prefix + T, 16-byte aligned.  result: device, as written
+ * by tsw_accept_greedy (read on the device; out-of-range entries are
+ * clamped, so no access leaves rows n_prefix .. n_prefix + T - 1).  All
+ * source rows are read before any is written.  Errors: TSW_EINVAL,
+ * TSW_EUNSUPPORTED (d other than 64/128, dtype), TSW_EHIP. */
+int tsw_kv_compact(void* k, void* v, int32_t n_layers, int64_t layer_stride, int32_t Hkv, int32_t d,
+                   int32_t dtype, int64_t kv_head_stride, int64_t n_prefix, int32_t T,
+                   const int32_t* result, tsw_stream_t stream);
+
 const char* tsw_status_str(int status);
 
 #ifdef __cplusplus

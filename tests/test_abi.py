@@ -153,3 +153,49 @@ def test_split_and_merge_argument_errors(L):
 
 def test_null_workspace(L):
     assert _verify(L, _desc(), ws=None) == EINVAL
+
+
+def test_accept_argument_errors(L):
+    p = PARENT.ctypes.data_as(ctypes.c_void_p)
+    call = lambda **kw: L.tsw_accept_greedy(
+        kw.get("parent", p), kw.get("T", 13), kw.get("logits", FAKE), kw.get("vocab", 1000),
+        kw.get("dtype", 0), kw.get("draft", FAKE), kw.get("result", FAKE), kw.get("ws", FAKE),
+        1 << 20, None)
+    assert call(T=0) == EINVAL
+    assert call(T=65) == EINVAL
+    assert call(vocab=0) == EINVAL
+    assert call(vocab=1 << 31) == EINVAL
+    assert call(parent=None) == EINVAL
+    bad = np.array([-1, 0, 5] + [0] * 10, dtype=np.int32)
+    assert call(parent=bad.ctypes.data_as(ctypes.c_void_p)) == EBADTREE
+    assert call(dtype=5) == EUNSUP
+    assert call(logits=None) == EINVAL
+    assert call(draft=None) == EINVAL
+    assert call(result=None) == EINVAL
+    assert call(ws=None) == EINVAL
+    assert call(ws=ctypes.c_void_p(0x10004)) == EINVAL      # not 8-byte aligned
+    n = ctypes.c_size_t(0)
+    assert L.tsw_accept_workspace_size(0, 100, ctypes.byref(n)) == EINVAL
+    assert L.tsw_accept_workspace_size(13, 0, ctypes.byref(n)) == EINVAL
+    assert L.tsw_accept_workspace_size(13, 100, None) == EINVAL
+
+
+def test_compact_argument_errors(L):
+    def call(**kw):
+        a = dict(k=FAKE, v=FAKE, layers=2, layer_stride=8 * 200 * 128, Hkv=8, d=128, dtype=1,
+                 hs=200 * 128, n_prefix=100, T=40, result=FAKE)
+        a.update(kw)
+        return L.tsw_kv_compact(a["k"], a["v"], a["layers"], a["layer_stride"], a["Hkv"], a["d"],
+                                a["dtype"], a["hs"], a["n_prefix"], a["T"], a["result"], None)
+    assert call(k=None) == EINVAL
+    assert call(result=None) == EINVAL
+    assert call(T=0) == EINVAL
+    assert call(T=65) == EINVAL
+    assert call(layers=0) == EINVAL
+    assert call(Hkv=0) == EINVAL
+    assert call(d=96) == EUNSUP
+    assert call(dtype=3) == EUNSUP
+    assert call(n_prefix=-1) == EINVAL
+    assert call(hs=100 * 128) == EINVAL                       # rows < n_prefix + T
+    assert call(layer_stride=8 * 200 * 128 - 1) == EINVAL     # layers overlap
+    assert call(k=ctypes.c_void_p(0x10008)) == EINVAL         # not 16-byte aligned

@@ -419,3 +419,23 @@ def test_hip_graph_replays_match_eager():
         assert torch.equal(o, o_e) and torch.equal(lse, l_e), rep
         assert torch.equal(op, op_e) and torch.equal(lp, lp_e), rep
     say("graph replays: 4 x bit-identical")
+
+
+@pytest.mark.parametrize("impl,npre", [("mfma", 5000), ("valu", 700), ("auto", 100)])
+def test_v_ones_gives_exactly_one(impl, npre):
+    """V = 1 everywhere: every output element is 1 up to float32 rounding of
+    the normalisation, because the row sum is taken over the same (rounded)
+    weights that multiply V; the LSE still matches the oracle."""
+    T, Hq, Hkv, d = 40, 32, 8, 128
+    parent = wl.kary_tree_parent(T, 3)
+    q = gen((T, Hq, d), 71, torch.bfloat16)
+    k = gen((Hkv, npre + T, d), 72, torch.bfloat16)
+    v = torch.ones((Hkv, npre + T, d), dtype=torch.bfloat16, device=q.device)
+    o, lse = tsw.tree_attn_verify(q, k, v, parent, npre, impl=impl)
+    torch.cuda.synchronize()
+    err = float((o - 1.0).abs().max())
+    say("V=1 %s: max|O-1| %.3g" % (impl, err))
+    assert err <= 2e-6
+    o_ref, l_ref = oracle.tree_attn(wl.oracle_view(q), wl.oracle_view(k), wl.oracle_view(v),
+                                    parent, npre, 1 / np.sqrt(d), nthreads=NTHREADS)
+    check(o, lse, o_ref, l_ref, TOL["bf16"], "V=1 %s" % impl)

@@ -57,11 +57,15 @@ def lib():
     L.tsw_tree_attn_partial.argtypes = [D, vp, vp, vp, vp, vp, i64, vp, vp, vp, sz, vp]
     L.tsw_tree_attn_split.argtypes = [D, vp, vp, vp, vp, vp, i64, i32, vp, vp, vp]
     L.tsw_lse_merge.argtypes = [i32, i64, i32, vp, vp, vp, vp, vp]
+    L.tsw_accept_workspace_size.argtypes = [i32, i64, ctypes.POINTER(sz)]
+    L.tsw_accept_greedy.argtypes = [vp, i32, vp, i64, i32, vp, vp, vp, sz, vp]
+    L.tsw_kv_compact.argtypes = [vp, vp, i32, i64, i32, i32, i32, i64, i64, i32, vp, vp]
     L.tsw_status_str.argtypes = [ctypes.c_int]
     L.tsw_status_str.restype = ctypes.c_char_p
     for name in ("tsw_tree_mask_build", "tsw_plan_splits", "tsw_workspace_size",
                  "tsw_tree_attn_verify", "tsw_tree_attn_partial", "tsw_tree_attn_split",
-                 "tsw_lse_merge"):
+                 "tsw_lse_merge", "tsw_accept_workspace_size", "tsw_accept_greedy",
+                 "tsw_kv_compact"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L
@@ -297,3 +301,90 @@ def prepare_merge(part_o, part_lse, o, lse, stream=None):
     args = (part_o.shape[0], part_lse[0].numel(), part_o.shape[-1], _dev_ptr(part_o),
             _dev_ptr(part_lse), _dev_ptr(o), _dev_ptr(lse), st)
     return PreparedCall(lib().tsw_lse_merge, args, "tsw_lse_merge", None)
+
+
+# ------------------------------------------------------------ acceptance
+
+def accept_workspace_size(T, vocab):
+    n = ctypes.c_size_t(0)
+    _check(lib().tsw_accept_workspace_size(int(T), int(vocab), ctypes.byref(n)),
+           "tsw_accept_workspace_size")
+    return n.value
+
+
+def _logits_dtype(logits):
+    if logits.dtype == torch.float32:
+        return DTYPE_F32
+    if logits.dtype == torch.bfloat16:
+        return DTYPE_BF16
+    raise TypeError("logits must be float32 or bfloat16")
+
+
+def _accept_args(parent, logits, draft, result, workspace, stream):
+    if logits.dim() != 2 or not logits.is_cuda or not logits.is_contiguous():
+        raise ValueError("logits must be a contiguous [T, vocab] GPU tensor")
+    T, vocab = logits.shape
+    if draft.dtype != torch.int32 or not draft.is_cuda or draft.numel() != T:
+        raise ValueError("draft must be an int32 GPU tensor of T entries")
+    p = _parent_arr(parent)
+    if p.shape[0] != T:
+        raise ValueError("parent must have T entries")
+    if result is None:
+        result = torch.empty(2 + 2 * T, dtype=torch.int32, device=logits.device)
+    if workspace is None:
+        workspace = torch.empty(max(accept_workspace_size(T, vocab), 256), dtype=torch.uint8,
+                                device=logits.device)
+    st = ctypes.c_void_p(stream.cuda_stream if stream is not None
+                         else torch.cuda.current_stream(logits.device).cuda_stream)
+    args = (_np_ptr(p), T, _dev_ptr(logits), vocab, _logits_dtype(logits), _dev_ptr(draft),
+            _dev_ptr(result), _dev_ptr(workspace), workspace.numel(), st)
+    return args, (p, result, workspace)
+
+
+def accept_greedy(parent, logits, draft, result=None, workspace=None):
+    """Greedy acceptance; returns the int32 device result [2 + 2T]:
+    (L, bonus, path[T] padded with -1, most likely token per node)."""
+    args, keep = _accept_args(parent, logits, draft, result, workspace, None)
+    _check(lib().tsw_accept_greedy(*args), "tsw_accept_greedy")
+    return keep[1]
+
+
+def prepare_accept(parent, logits, draft, result, workspace, stream=None):
+    args, keep = _accept_args(parent, logits, draft, result, workspace, stream)
+    return PreparedCall(lib().tsw_accept_greedy, args, "tsw_accept_greedy", keep)
+
+
+def _compact_args(k, v, n_prefix, T, result, stream):
+    if k.shape != v.shape or k.dtype != v.dtype or not (k.is_cuda and v.is_cuda):
+        raise ValueError("k and v must be GPU tensors of one shape and dtype")
+    if k.dim() == 3:
+        n_layers, layer_stride = 1, 0
+        Hkv, rows, d = k.shape
+        hs = k.stride(0)
+    elif k.dim() == 4:
+        n_layers, Hkv, rows, d = k.shape
+        layer_stride, hs = k.stride(0), k.stride(1)
+        if v.stride(0) != layer_stride:
+            raise ValueError("k and v must share strides")
+    else:
+        raise ValueError("k, v must be [Hkv, rows, d] or [layers, Hkv, rows, d]")
+    if k.stride(-1) != 1 or k.stride(-2) != d or v.stride(-1) != 1 or v.stride(-2) != d \
+            or v.stride(-3) != hs:
+        raise ValueError("k and v rows must be contiguous with equal head strides")
+    if rows < int(n_prefix) + int(T):
+        raise ValueError("the caches need n_prefix + T rows")
+    dt = DTYPE_F32 if k.dtype == torch.float32 else DTYPE_BF16
+    st = ctypes.c_void_p(stream.cuda_stream if stream is not None
+                         else torch.cuda.current_stream(k.device).cuda_stream)
+    return (_dev_ptr(k), _dev_ptr(v), n_layers, layer_stride, Hkv, d, dt, hs, int(n_prefix), int(T),
+            _dev_ptr(result), st)
+
+
+def kv_compact(k, v, n_prefix, T, result):
+    """Move the accepted path's K/V rows in place (see tsw_kv_compact)."""
+    _check(lib().tsw_kv_compact(*_compact_args(k, v, n_prefix, T, result, None)), "tsw_kv_compact")
+
+
+def prepare_compact(k, v, n_prefix, T, result, stream=None):
+    return PreparedCall(lib().tsw_kv_compact, _compact_args(k, v, n_prefix, T, result, stream),
+                        "tsw_kv_compact", (k, v, result))

@@ -1,0 +1,184 @@
+// Greedy acceptance of a verified draft tree and compaction of the accepted
+// path's K/V rows (gfx950).
+//
+// After the verification pass the target model's logits at every tree node
+// give its most likely next token there; a drafted node is kept when its
+// parent is kept and its token equals that prediction at the parent, and the
+// longest kept root path becomes the output.  Sources: "TokenSwift - A
+// framework for accelerating the generation of ultra-long text" (aiboss88
+// project page), technical principles, tree-based multi-candidate token
+// verification (the longest valid n-gram is kept, consistent with the target
+// model); Tencent Cloud article "90分钟生成10万Token，新框架实现3倍无损加速超长
+// 文本生成", 技术原理, parallel-verification figure text (the longest valid
+// candidate is selected after checking against the full KV cache).
+//
+// Three kernels:
+//   argmax_partial  grid (chunks, T): each work-group scans one slice of one
+//                   node's logits with 16-byte loads and keeps the largest
+//                   value (first index among equals).  HBM-bound.
+//   accept_walk     one work-group: folds the slices per node, then walks
+//                   the tree in node order (parents before children).
+//   kv_compact      grid (kv head, layer, K|V): moves the accepted path's
+//                   rows to n_prefix, n_prefix + 1, ...; all sources are read
+//                   into LDS before any destination is written, since a
+//                   destination row can be the source of an earlier move.
+#include <limits.h>
+
+#include "tsw_device.h"
+#include "tsw_internal.h"
+
+namespace tsw {
+
+namespace {
+
+// (value, index) with the larger value winning and the lower index breaking
+// ties.  An unset pair has index INT_MAX, so any element beats it.
+struct Best {
+    float v;
+    int i;
+};
+
+__device__ __forceinline__ Best better(Best a, Best b) {
+    if (b.v > a.v || (b.v == a.v && b.i < a.i)) return b;
+    return a;
+}
+
+__device__ __forceinline__ Best wave_best(Best x) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) {
+        Best y;
+        y.v = __shfl_xor(x.v, m);
+        y.i = __shfl_xor(x.i, m);
+        x = better(x, y);
+    }
+    return x;
+}
+
+__device__ __forceinline__ float widen(float x) { return x; }
+__device__ __forceinline__ float widen(__bf16 x) { return (float)x; }
+
+template <typename TIN>
+__global__ __launch_bounds__(256) void argmax_partial(const TIN* __restrict__ logits, int64_t vocab,
+                                                      int64_t chunk, int n_chunks, bool vec_ok,
+                                                      AcceptPartial* __restrict__ part) {
+    constexpr int VEC = 16 / sizeof(TIN);
+    const int t = blockIdx.y;
+    const int c = blockIdx.x;
+    const TIN* row = logits + (int64_t)t * vocab;
+    const int64_t start = (int64_t)c * chunk;
+    const int64_t end = start + chunk < vocab ? start + chunk : vocab;
+    Best b{-INFINITY, INT_MAX};
+    if (vec_ok) {
+        // start and the row are 16-byte aligned: whole vectors, then the tail
+        const int64_t vend = start + ((end - start) / VEC) * VEC;
+        for (int64_t i = start + (int64_t)threadIdx.x * VEC; i < vend; i += 256 * VEC) {
+            typedef TIN vec_t __attribute__((ext_vector_type(VEC)));
+            const vec_t x = *(const vec_t*)(row + i);
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) b = better(b, Best{widen(x[e]), (int)(i + e)});
+        }
+        for (int64_t i = vend + threadIdx.x; i < end; i += 256) b = better(b, Best{widen(row[i]), (int)i});
+    } else {
+        for (int64_t i = start + threadIdx.x; i < end; i += 256) b = better(b, Best{widen(row[i]), (int)i});
+    }
+    b = wave_best(b);
+    __shared__ Best wb[4];
+    if ((threadIdx.x & 63) == 0) wb[threadIdx.x >> 6] = b;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        Best r = better(better(wb[0], wb[1]), better(wb[2], wb[3]));
+        part[(int64_t)t * n_chunks + c] = AcceptPartial{r.v, r.i};
+    }
+}
+
+__global__ __launch_bounds__(64) void accept_walk(const AcceptArgs a, const AcceptPartial* __restrict__ part,
+                                                  const int32_t* __restrict__ draft, int32_t* __restrict__ result) {
+    __shared__ int tgt[64];
+    const int t = threadIdx.x;
+    if (t < a.T) {
+        Best b{-INFINITY, INT_MAX};
+        for (int c = 0; c < a.n_chunks; ++c) {
+            const AcceptPartial p = part[(int64_t)t * a.n_chunks + c];
+            b = better(b, Best{p.v, p.i});
+        }
+        // all-NaN rows leave no index: report token 0 (NaN logits are outside
+        // the contract)
+        const int tok = b.i == INT_MAX ? 0 : b.i;
+        tgt[t] = tok;
+        result[2 + a.T + t] = tok;
+    }
+    __syncthreads();
+    if (t == 0) {
+        bool acc[64];
+        int dep[64];
+        acc[0] = true;
+        dep[0] = 0;
+        int best = 0;
+        for (int i = 1; i < a.T; ++i) {
+            const int p = a.parent[i];
+            acc[i] = acc[p] && draft[i] == tgt[p];
+            dep[i] = dep[p] + 1;
+            if (acc[i] && dep[i] > dep[best]) best = i;
+        }
+        const int L = dep[best] + 1;
+        int node = best;
+        for (int k = L - 1; k >= 0; --k) {
+            result[2 + k] = node;
+            node = a.parent[node];
+        }
+        for (int k = L; k < a.T; ++k) result[2 + k] = -1;
+        result[0] = L;
+        result[1] = tgt[best];
+    }
+}
+
+// One (kv head, layer, K or V) per work-group.  Row bytes RB = d * element
+// size (128, 256 or 512), moved in 16-byte pieces.
+__global__ __launch_bounds__(256) void kv_compact(const CompactArgs a, const int32_t* __restrict__ result) {
+    __shared__ uint4 stage[63 * 32];                 // up to 63 moved rows of <= 512 bytes
+    const int head = blockIdx.x;
+    const int layer = blockIdx.y;
+    char* base = (char*)(blockIdx.z == 0 ? a.k : a.v) + ((int64_t)layer * a.layer_stride +
+                                                         (int64_t)head * a.kv_head_stride) * a.esz;
+    int L = result[0];
+    L = L < 1 ? 1 : (L > a.T ? a.T : L);
+    const int pieces = a.row_bytes / 16;
+    const int n = (L - 1) * pieces;                  // row 0 (the root) never moves
+    for (int e = threadIdx.x; e < n; e += 256) {
+        const int k = 1 + e / pieces;
+        int src = result[2 + k];
+        src = src < 0 ? 0 : (src >= a.T ? a.T - 1 : src);
+        stage[e] = *(const uint4*)(base + (a.n_prefix + src) * a.row_bytes + (e % pieces) * 16);
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < n; e += 256) {
+        const int k = 1 + e / pieces;
+        *(uint4*)(base + (a.n_prefix + k) * a.row_bytes + (e % pieces) * 16) = stage[e];
+    }
+}
+
+}  // namespace
+
+hipError_t launch_accept(const AcceptArgs& a, const void* logits, int logits_dtype, int64_t vocab, int64_t chunk,
+                         bool vec_ok, const int32_t* draft, int32_t* result, AcceptPartial* part,
+                         hipStream_t stream) {
+    const dim3 grid(a.n_chunks, a.T);
+    if (logits_dtype == 0)
+        hipLaunchKernelGGL(argmax_partial<float>, grid, dim3(256), 0, stream, (const float*)logits, vocab, chunk,
+                           a.n_chunks, vec_ok, part);
+    else
+        hipLaunchKernelGGL(argmax_partial<__bf16>, grid, dim3(256), 0, stream, (const __bf16*)logits, vocab, chunk,
+                           a.n_chunks, vec_ok, part);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(accept_walk, dim3(1), dim3(64), 0, stream, a, part, draft, result);
+    return hipGetLastError();
+}
+
+hipError_t launch_kv_compact(const CompactArgs& a, int n_layers, int n_kv_heads, const int32_t* result,
+                             hipStream_t stream) {
+    hipLaunchKernelGGL(kv_compact, dim3(n_kv_heads, n_layers, 2), dim3(256), 0, stream, a, result);
+    return hipGetLastError();
+}
+
+}  // namespace tsw

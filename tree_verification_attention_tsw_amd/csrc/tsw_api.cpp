@@ -1,6 +1,7 @@
 // Host side of the tree-verification attention library: argument checks,
 // the tree mask builder, the split planner and the C entry points declared
-// in include/tsw.h.  Kernels live in tsw_kernels.hip.
+// in include/tsw.h.  Kernels live in tsw_kernels.hip, tsw_mfma*.hip and
+// tsw_accept.hip.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -215,6 +216,27 @@ int full_call(const tsw_attn_desc* d, const void* q, const void* k, const void* 
                                             (hipStream_t)stream));
 }
 
+// Logit slices for the acceptance argmax: about two work-groups per CU over
+// all nodes, each slice a multiple of 2048 elements (whole 16-byte vectors
+// for every lane of a 256-thread work-group).
+constexpr int64_t kAcceptSliceQuantum = 2048;
+
+int accept_plan(int32_t T, int64_t vocab, int64_t* chunk, int32_t* n_chunks) {
+    int cus = 0;
+    int rc = device_cus(&cus);
+    if (rc != TSW_OK) return rc;
+    const int64_t per_node = cdiv(2 * (int64_t)cus, T);
+    *chunk = cdiv(cdiv(vocab, per_node), kAcceptSliceQuantum) * kAcceptSliceQuantum;
+    *n_chunks = (int32_t)cdiv(vocab, *chunk);
+    return TSW_OK;
+}
+
+int check_accept_shape(int32_t T, int64_t vocab) {
+    if (T < 1 || T > kMaxNodes) return TSW_EINVAL;
+    if (vocab < 1 || vocab > INT32_MAX) return TSW_EINVAL;
+    return TSW_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -277,6 +299,69 @@ int tsw_lse_merge(int32_t n_splits, int64_t n_rows, int32_t d, const float* part
     if (n_rows > 0 && (!part_o || !part_lse || !o || !lse)) return TSW_EINVAL;
     return hip_status(tsw::launch_lse_merge(n_splits, n_rows, d, part_o, part_lse, o, lse,
                                             (hipStream_t)stream));
+}
+
+int tsw_accept_workspace_size(int32_t T, int64_t vocab, size_t* bytes) {
+    if (!bytes) return TSW_EINVAL;
+    int rc = check_accept_shape(T, vocab);
+    if (rc != TSW_OK) return rc;
+    int64_t chunk = 0;
+    int32_t n_chunks = 0;
+    rc = accept_plan(T, vocab, &chunk, &n_chunks);
+    if (rc != TSW_OK) return rc;
+    *bytes = align256((size_t)T * n_chunks * sizeof(tsw::AcceptPartial));
+    return TSW_OK;
+}
+
+int tsw_accept_greedy(const int32_t* parent, int32_t T, const void* logits, int64_t vocab, int32_t logits_dtype,
+                      const int32_t* draft, int32_t* result, void* workspace, size_t workspace_bytes,
+                      tsw_stream_t stream) {
+    int rc = check_accept_shape(T, vocab);
+    if (rc != TSW_OK) return rc;
+    uint64_t mask[kMaxNodes];
+    rc = build_mask(parent, T, mask, nullptr);
+    if (rc != TSW_OK) return rc;
+    if (logits_dtype != TSW_DTYPE_F32 && logits_dtype != TSW_DTYPE_BF16) return TSW_EUNSUPPORTED;
+    if (!logits || !draft || !result || !workspace) return TSW_EINVAL;
+    if ((uintptr_t)workspace & 7) return TSW_EINVAL;
+    int64_t chunk = 0;
+    tsw::AcceptArgs a;
+    memset(&a, 0, sizeof a);
+    rc = accept_plan(T, vocab, &chunk, &a.n_chunks);
+    if (rc != TSW_OK) return rc;
+    if (workspace_bytes < (size_t)T * a.n_chunks * sizeof(tsw::AcceptPartial)) return TSW_ENOSPACE;
+    a.T = T;
+    for (int i = 0; i < T; ++i) a.parent[i] = parent[i];
+    const int64_t esz = logits_dtype == TSW_DTYPE_F32 ? 4 : 2;
+    const bool vec_ok = ((uintptr_t)logits & 15) == 0 && (vocab * esz) % 16 == 0;
+    return hip_status(tsw::launch_accept(a, logits, logits_dtype == TSW_DTYPE_F32 ? 0 : 1, vocab, chunk, vec_ok,
+                                         draft, result, (tsw::AcceptPartial*)workspace, (hipStream_t)stream));
+}
+
+int tsw_kv_compact(void* k, void* v, int32_t n_layers, int64_t layer_stride, int32_t Hkv, int32_t d, int32_t dtype,
+                   int64_t kv_head_stride, int64_t n_prefix, int32_t T, const int32_t* result,
+                   tsw_stream_t stream) {
+    if (!k || !v || !result) return TSW_EINVAL;
+    if (T < 1 || T > kMaxNodes || n_layers < 1 || n_layers > 65535 || Hkv < 1 || Hkv > 65535) return TSW_EINVAL;
+    if (d != 64 && d != 128) return TSW_EUNSUPPORTED;
+    if (dtype != TSW_DTYPE_F32 && dtype != TSW_DTYPE_BF16) return TSW_EUNSUPPORTED;
+    if (n_prefix < 0) return TSW_EINVAL;
+    if (kv_head_stride < (n_prefix + T) * d) return TSW_EINVAL;
+    if (n_layers > 1 && layer_stride < (int64_t)Hkv * kv_head_stride) return TSW_EINVAL;
+    const int esz = dtype == TSW_DTYPE_F32 ? 4 : 2;
+    if (((uintptr_t)k | (uintptr_t)v) & 15) return TSW_EINVAL;
+    if ((kv_head_stride * esz) % 16 || (layer_stride * esz) % 16) return TSW_EINVAL;
+    tsw::CompactArgs a;
+    memset(&a, 0, sizeof a);
+    a.k = k;
+    a.v = v;
+    a.layer_stride = n_layers > 1 ? layer_stride : 0;
+    a.kv_head_stride = kv_head_stride;
+    a.n_prefix = n_prefix;
+    a.T = T;
+    a.esz = esz;
+    a.row_bytes = d * esz;
+    return hip_status(tsw::launch_kv_compact(a, n_layers, Hkv, result, (hipStream_t)stream));
 }
 
 const char* tsw_status_str(int status) {

@@ -1,5 +1,6 @@
 // Internal interface between the host API (tsw_api.cpp) and the gfx950
-// kernels (tsw_kernels.hip).  Not part of the public ABI.
+// kernels (tsw_kernels.hip, tsw_mfma*.hip, tsw_accept.hip).  Not part of the
+// public ABI.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -48,6 +49,31 @@ hipError_t launch_split_valu(int dtype, int d, bool gather, const SplitArgs& a, 
                              hipStream_t stream);
 hipError_t launch_lse_merge(int n_splits, int64_t n_rows, int d, const float* part_o,
                             const float* part_lse, float* o, float* lse, hipStream_t stream);
+
+// Greedy acceptance: per-slice maxima of one node's logits, the tree (in the
+// kernel arguments, like the mask above) and the slice count.
+struct AcceptPartial {
+    float v;
+    int32_t i;
+};
+struct AcceptArgs {
+    int32_t T, n_chunks;
+    int32_t parent[64];
+};
+// Accepted-path compaction of one cache (n_layers x Hkv heads of K and V).
+struct CompactArgs {
+    void* k;
+    void* v;
+    int64_t layer_stride;    // elements between layers
+    int64_t kv_head_stride;  // elements between kv heads
+    int64_t n_prefix;        // tree node j sits at row n_prefix + j
+    int32_t T, esz, row_bytes;
+};
+hipError_t launch_accept(const AcceptArgs& a, const void* logits, int logits_dtype, int64_t vocab, int64_t chunk,
+                         bool vec_ok, const int32_t* draft, int32_t* result, AcceptPartial* part,
+                         hipStream_t stream);
+hipError_t launch_kv_compact(const CompactArgs& a, int n_layers, int n_kv_heads, const int32_t* result,
+                             hipStream_t stream);
 
 // Key tile of the vector-ALU kernel and its query rows per work-group.
 constexpr int kValuTile = 64;
