@@ -16,8 +16,8 @@
 //   argmax_partial  grid (chunks, T): each work-group scans one slice of one
 //                   node's logits with 16-byte loads and keeps the largest
 //                   value (first index among equals).  HBM-bound.
-//   accept_walk     one work-group: folds the slices per node, then walks
-//                   the tree in node order (parents before children).
+//   accept_walk     one wavefront (lane = node): folds the slices per node,
+//                   then finds the accepted nodes by pointer jumping.
 //   kv_compact      grid (kv head, layer, K|V): moves the accepted path's
 //                   rows to n_prefix, n_prefix + 1, ...; all sources are read
 //                   into LDS before any destination is written, since a
@@ -69,15 +69,27 @@ __global__ __launch_bounds__(256) void argmax_partial(const TIN* __restrict__ lo
     const int64_t end = start + chunk < vocab ? start + chunk : vocab;
     Best b{-INFINITY, INT_MAX};
     if (vec_ok) {
-        // start and the row are 16-byte aligned: whole vectors, then the tail
+        // start and the row are 16-byte aligned: whole vectors (four loads in
+        // flight per lane), then the tail
+        typedef TIN vec_t __attribute__((ext_vector_type(VEC)));
+        constexpr int64_t STEP = 256 * VEC;
         const int64_t vend = start + ((end - start) / VEC) * VEC;
-        for (int64_t i = start + (int64_t)threadIdx.x * VEC; i < vend; i += 256 * VEC) {
-            typedef TIN vec_t __attribute__((ext_vector_type(VEC)));
+        int64_t i = start + (int64_t)threadIdx.x * VEC;
+        for (; i + 3 * STEP < vend; i += 4 * STEP) {
+            vec_t x[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) x[u] = *(const vec_t*)(row + i + u * STEP);
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+#pragma unroll
+                for (int e = 0; e < VEC; ++e) b = better(b, Best{widen(x[u][e]), (int)(i + u * STEP + e)});
+        }
+        for (; i < vend; i += STEP) {
             const vec_t x = *(const vec_t*)(row + i);
 #pragma unroll
             for (int e = 0; e < VEC; ++e) b = better(b, Best{widen(x[e]), (int)(i + e)});
         }
-        for (int64_t i = vend + threadIdx.x; i < end; i += 256) b = better(b, Best{widen(row[i]), (int)i});
+        for (int64_t j = vend + threadIdx.x; j < end; j += 256) b = better(b, Best{widen(row[j]), (int)j});
     } else {
         for (int64_t i = start + threadIdx.x; i < end; i += 256) b = better(b, Best{widen(row[i]), (int)i});
     }
@@ -91,11 +103,18 @@ __global__ __launch_bounds__(256) void argmax_partial(const TIN* __restrict__ lo
     }
 }
 
+// One wavefront, lane i = node i.  A node agrees with the target when its
+// draft token is the most likely token at its parent; it is accepted when
+// every node on its root path agrees, found by pointer jumping (six steps
+// cover depth 63).  The deepest accepted node (lowest index among equals)
+// is picked by a wave reduction, and its ancestor-or-self bits give the path
+// (the node at depth k is path entry k).
 __global__ __launch_bounds__(64) void accept_walk(const AcceptArgs a, const AcceptPartial* __restrict__ part,
                                                   const int32_t* __restrict__ draft, int32_t* __restrict__ result) {
-    __shared__ int tgt[64];
     const int t = threadIdx.x;
-    if (t < a.T) {
+    const bool live = t < a.T;
+    int tok = 0;
+    if (live) {
         Best b{-INFINITY, INT_MAX};
         for (int c = 0; c < a.n_chunks; ++c) {
             const AcceptPartial p = part[(int64_t)t * a.n_chunks + c];
@@ -103,32 +122,34 @@ __global__ __launch_bounds__(64) void accept_walk(const AcceptArgs a, const Acce
         }
         // all-NaN rows leave no index: report token 0 (NaN logits are outside
         // the contract)
-        const int tok = b.i == INT_MAX ? 0 : b.i;
-        tgt[t] = tok;
+        tok = b.i == INT_MAX ? 0 : b.i;
         result[2 + a.T + t] = tok;
     }
-    __syncthreads();
+    const int par = live && t > 0 ? a.parent[t] : 0;
+    const int parent_tok = __shfl(tok, par);
+    int ok = live && (t == 0 || draft[t] == parent_tok);
+    int anc = par;
+#pragma unroll
+    for (int step = 0; step < 6; ++step) {
+        ok = ok & __shfl(ok, anc);
+        anc = __shfl(anc, anc);
+    }
+    const int depth = live ? a.depth[t] : 0;
+    // key: deeper first, then lower index; -1 for nodes not accepted
+    int key = ok ? (depth << 8) | (255 - t) : -1;
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) key = max(key, __shfl_xor(key, m));
+    const int best = 255 - (key & 255);               // the root is always accepted, so key >= 0
+    const int L = (key >> 8) + 1;
+    const uint64_t on_path = a.mask[best];
+    const int bonus = __shfl(tok, best);
+    if (live) {
+        if ((on_path >> t) & 1ull) result[2 + depth] = t;
+        if (t >= L) result[2 + t] = -1;
+    }
     if (t == 0) {
-        bool acc[64];
-        int dep[64];
-        acc[0] = true;
-        dep[0] = 0;
-        int best = 0;
-        for (int i = 1; i < a.T; ++i) {
-            const int p = a.parent[i];
-            acc[i] = acc[p] && draft[i] == tgt[p];
-            dep[i] = dep[p] + 1;
-            if (acc[i] && dep[i] > dep[best]) best = i;
-        }
-        const int L = dep[best] + 1;
-        int node = best;
-        for (int k = L - 1; k >= 0; --k) {
-            result[2 + k] = node;
-            node = a.parent[node];
-        }
-        for (int k = L; k < a.T; ++k) result[2 + k] = -1;
         result[0] = L;
-        result[1] = tgt[best];
+        result[1] = bonus;
     }
 }
 

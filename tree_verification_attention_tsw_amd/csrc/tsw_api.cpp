@@ -216,16 +216,16 @@ int full_call(const tsw_attn_desc* d, const void* q, const void* k, const void* 
                                             (hipStream_t)stream));
 }
 
-// Logit slices for the acceptance argmax: about two work-groups per CU over
-// all nodes, each slice a multiple of 2048 elements (whole 16-byte vectors
-// for every lane of a 256-thread work-group).
+// Logit slices for the acceptance argmax: about four work-groups per CU
+// over all nodes, each slice a multiple of 2048 elements (whole 16-byte
+// vectors for every lane of a 256-thread work-group).
 constexpr int64_t kAcceptSliceQuantum = 2048;
 
 int accept_plan(int32_t T, int64_t vocab, int64_t* chunk, int32_t* n_chunks) {
     int cus = 0;
     int rc = device_cus(&cus);
     if (rc != TSW_OK) return rc;
-    const int64_t per_node = cdiv(2 * (int64_t)cus, T);
+    const int64_t per_node = cdiv(4 * (int64_t)cus, T);
     *chunk = cdiv(cdiv(vocab, per_node), kAcceptSliceQuantum) * kAcceptSliceQuantum;
     *n_chunks = (int32_t)cdiv(vocab, *chunk);
     return TSW_OK;
@@ -318,15 +318,14 @@ int tsw_accept_greedy(const int32_t* parent, int32_t T, const void* logits, int6
                       tsw_stream_t stream) {
     int rc = check_accept_shape(T, vocab);
     if (rc != TSW_OK) return rc;
-    uint64_t mask[kMaxNodes];
-    rc = build_mask(parent, T, mask, nullptr);
+    tsw::AcceptArgs a;
+    memset(&a, 0, sizeof a);
+    rc = build_mask(parent, T, a.mask, a.depth);
     if (rc != TSW_OK) return rc;
     if (logits_dtype != TSW_DTYPE_F32 && logits_dtype != TSW_DTYPE_BF16) return TSW_EUNSUPPORTED;
     if (!logits || !draft || !result || !workspace) return TSW_EINVAL;
     if ((uintptr_t)workspace & 7) return TSW_EINVAL;
     int64_t chunk = 0;
-    tsw::AcceptArgs a;
-    memset(&a, 0, sizeof a);
     rc = accept_plan(T, vocab, &chunk, &a.n_chunks);
     if (rc != TSW_OK) return rc;
     if (workspace_bytes < (size_t)T * a.n_chunks * sizeof(tsw::AcceptPartial)) return TSW_ENOSPACE;

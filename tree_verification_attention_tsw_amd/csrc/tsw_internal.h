@@ -50,8 +50,9 @@ hipError_t launch_split_valu(int dtype, int d, bool gather, const SplitArgs& a, 
 hipError_t launch_lse_merge(int n_splits, int64_t n_rows, int d, const float* part_o,
                             const float* part_lse, float* o, float* lse, hipStream_t stream);
 
-// Greedy acceptance: per-slice maxima of one node's logits, the tree (in the
-// kernel arguments, like the mask above) and the slice count.
+// Greedy acceptance: per-slice maxima of one node's logits, the tree with
+// depths and ancestor-or-self bits (in the kernel arguments, like the mask
+// above) and the slice count.
 struct AcceptPartial {
     float v;
     int32_t i;
@@ -59,6 +60,8 @@ struct AcceptPartial {
 struct AcceptArgs {
     int32_t T, n_chunks;
     int32_t parent[64];
+    int32_t depth[64];
+    uint64_t mask[64];       // ancestor-or-self bits per node
 };
 // Accepted-path compaction of one cache (n_layers x Hkv heads of K and V).
 struct CompactArgs {

@@ -130,6 +130,53 @@ WORKLOADS = {
 }
 
 
+@dataclass
+class AcceptWorkload:
+    """Acceptance of one verified tree and compaction of every layer's cache."""
+    name: str
+    n_nodes: int
+    vocab: int
+    logits_dtype: str
+    layers: int
+    Hkv: int
+    d: int
+    n_prefix: int
+    seed: int
+    p_match: float = 0.8
+
+    def parent(self) -> np.ndarray:
+        return kary_tree_parent(self.n_nodes, 3)
+
+    def logits_bytes(self) -> int:
+        return self.n_nodes * self.vocab * (4 if self.logits_dtype == F32 else 2)
+
+
+ACCEPT_WORKLOADS = {
+    # LLaMA3.1-8B: 128256-token vocabulary, 32 layers, 8 kv heads of 128
+    "accept_llama8b": AcceptWorkload("accept_llama8b", n_nodes=full_kary_nodes(3), vocab=128256,
+                                     logits_dtype=F32, layers=32, Hkv=8, d=128, n_prefix=102400,
+                                     seed=7000),
+}
+
+
+def make_accept_inputs(w: AcceptWorkload, device, seed_offset: int = 0):
+    """Logits ~ N(0, 1) and draft tokens that repeat the most likely token at
+    the parent with probability p_match (else a uniform token)."""
+    g = torch.Generator(device=device)
+    g.manual_seed(w.seed + seed_offset)
+    logits = torch.randn((w.n_nodes, w.vocab), generator=g, device=device, dtype=torch.float32)
+    if w.logits_dtype == BF16:
+        logits = logits.to(torch.bfloat16)
+    best = logits.float().argmax(dim=1).cpu().numpy()
+    rng = np.random.default_rng(w.seed + seed_offset)
+    parent = w.parent()
+    draft = rng.integers(0, w.vocab, size=w.n_nodes).astype(np.int32)
+    for i in range(1, w.n_nodes):
+        if rng.random() < w.p_match:
+            draft[i] = best[parent[i]]
+    return logits, torch.from_numpy(draft).to(device)
+
+
 def torch_dtype(dtype: str):
     return torch.float32 if dtype == F32 else torch.bfloat16
 
