@@ -153,6 +153,46 @@ int tsw_lse_merge(int32_t n_splits, int64_t n_rows, int32_t d, const float* part
 
 /* Static description of a status code. */
 /* ---------------------------------------------------------------------
+ * Paged batch: B sequences that share one tree shape (same T and parent[])
+ * but each have their own committed length n_prefix[b] and their own queries,
+ * with K and V stored in fixed-size pages of one pool.  Per sequence the
+ * result is exactly tsw_tree_attn_verify's on that sequence's cache.
+ *   q      [B][T][Hq][d]                        device
+ *   k_pages, v_pages [n_pages][Hkv][page_rows][d]  device page pools
+ *   block_table [B][max_pages] int32            device; sequence b's cache
+ *          position p lives in page block_table[b*max_pages + p/page_rows],
+ *          row p % page_rows; node j of the tree at position n_prefix[b] + j
+ *   n_prefix [B] int64                          HOST
+ *   o [B][T][Hq][d], lse [B][T][Hq] float32     device
+ * Only the matrix-core kernel serves this call (bfloat16, d = 128, at most
+ * 384 query rows per kv head): P is rounded to bfloat16 before P V, so with
+ * fewer than a few hundred visible keys the error can exceed that of the
+ * vector-ALU kernel.  The block-table entries a sequence needs must name
+ * pages of the pool (a precondition; they are read on the device).
+ * ------------------------------------------------------------------- */
+typedef struct tsw_paged_desc {
+    int32_t B;              /* sequences, 1..64 */
+    int32_t T, Hq, Hkv;     /* as in tsw_attn_desc */
+    int32_t d;              /* 128 */
+    int32_t page_rows;      /* rows per page: a power of two, 16..4096 */
+    int32_t max_pages;      /* entries per block-table row, >= ceil((n_prefix[b]+T)/page_rows) */
+    int32_t dtype;          /* TSW_DTYPE_BF16 */
+    float scale;            /* positive and finite */
+    int32_t reserved;       /* must be 0 */
+} tsw_paged_desc;
+
+/* Workspace bytes for a paged call with these lengths on the current device. */
+int tsw_paged_workspace_size(const tsw_paged_desc* desc, const int64_t* n_prefix, size_t* bytes);
+
+/* Errors: TSW_EINVAL (shape, lengths, pointers, alignment: q/k/v 16 bytes,
+ * workspace 256), TSW_EBADTREE, TSW_EUNSUPPORTED (dtype, d, too many rows
+ * per kv head), TSW_ENOSPACE, TSW_EHIP. */
+int tsw_tree_attn_verify_paged(const tsw_paged_desc* desc, const void* q, const void* k_pages,
+                               const void* v_pages, const int32_t* block_table,
+                               const int64_t* n_prefix, const int32_t* parent, float* o, float* lse,
+                               void* workspace, size_t workspace_bytes, tsw_stream_t stream);
+
+/* ---------------------------------------------------------------------
  * After verification: greedy acceptance and accepted-path KV compaction.
  *
  * The target model's logits at each tree node give its most likely next

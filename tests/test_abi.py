@@ -199,3 +199,40 @@ def test_compact_argument_errors(L):
     assert call(hs=100 * 128) == EINVAL                       # rows < n_prefix + T
     assert call(layer_stride=8 * 200 * 128 - 1) == EINVAL     # layers overlap
     assert call(k=ctypes.c_void_p(0x10008)) == EINVAL         # not 16-byte aligned
+
+
+def _pdesc(**kw):
+    d = tsw.PagedDesc(B=3, T=13, Hq=8, Hkv=2, d=128, page_rows=16, max_pages=20, dtype=tsw.DTYPE_BF16,
+                      scale=0.088, reserved=0)
+    for k, v in kw.items():
+        setattr(d, k, v)
+    return d
+
+
+def _paged(L, desc, npf=(100, 200, 0), q=FAKE, table=FAKE, ws=FAKE):
+    n = np.ascontiguousarray(np.asarray(npf, dtype=np.int64))
+    return L.tsw_tree_attn_verify_paged(ctypes.byref(desc), q, FAKE, FAKE, table,
+                                        n.ctypes.data_as(ctypes.c_void_p),
+                                        PARENT.ctypes.data_as(ctypes.c_void_p), FAKE, FAKE, ws, 1 << 30,
+                                        None)
+
+
+@pytest.mark.parametrize("field,value,code", [
+    ("B", 0, EINVAL), ("B", 65, EINVAL), ("T", 0, EINVAL), ("Hq", 3, EINVAL), ("d", 64, EUNSUP),
+    ("dtype", 0, EUNSUP), ("page_rows", 24, EINVAL), ("page_rows", 8, EINVAL), ("page_rows", 8192, EINVAL),
+    ("max_pages", 13, EINVAL), ("scale", 0.0, EINVAL), ("reserved", 1, EINVAL), ("Hq", 64, EUNSUP)])
+def test_paged_desc_errors(L, field, value, code):
+    npf = (100, 200, 0)
+    if field == "Hq" and value == 64:       # 13 * 32 = 416 rows per kv head: no matrix shape
+        assert _paged(L, _pdesc(Hq=64, Hkv=2), npf) == code
+        return
+    assert _paged(L, _pdesc(**{field: value}), npf) == code
+
+
+def test_paged_argument_errors(L):
+    assert _paged(L, _pdesc(), npf=(100, -1, 0)) == EINVAL
+    assert _paged(L, _pdesc(), q=None) == EINVAL
+    assert _paged(L, _pdesc(), table=None) == EINVAL
+    assert _paged(L, _pdesc(), q=ctypes.c_void_p(0x10008)) == EINVAL
+    n = ctypes.c_size_t(0)
+    assert L.tsw_paged_workspace_size(ctypes.byref(_pdesc(B=0)), None, ctypes.byref(n)) == EINVAL

@@ -1,0 +1,111 @@
+"""GPU parity of the paged batch call: every sequence's rows against the
+float64 oracle on that sequence's cache, rebuilt contiguously from the pages
+(K and V pages shuffled in the pool, sequences of different lengths)."""
+import os
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import tree_verification_attention_tsw_amd as tsw
+from tree_verification_attention_tsw_amd import workloads as wl
+
+pytestmark = pytest.mark.gpu
+TOL = 4e-3
+NTHREADS = min(16, len(os.sched_getaffinity(0)))
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    tsw.lib()
+
+
+def make_batch(lengths, T, Hq, Hkv, page_rows, seed, spare_pages=7):
+    d = 128
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed)
+    need = [-(-(n + T) // page_rows) for n in lengths]
+    n_pages = sum(need) + spare_pages
+    kp = torch.randn((n_pages, Hkv, page_rows, d), generator=g, device="cuda").to(torch.bfloat16)
+    vp = torch.randn((n_pages, Hkv, page_rows, d), generator=g, device="cuda").to(torch.bfloat16)
+    q = torch.randn((len(lengths), T, Hq, d), generator=g, device="cuda").to(torch.bfloat16)
+    perm = np.random.default_rng(seed).permutation(n_pages).astype(np.int32)
+    max_pages = max(need) + 2
+    table = np.full((len(lengths), max_pages), -1, dtype=np.int32)    # unused entries are never read
+    at = 0
+    for b, k in enumerate(need):
+        table[b, :k] = perm[at:at + k]
+        at += k
+    return q, kp, vp, torch.from_numpy(table).cuda(), table
+
+
+def contiguous(pool, table_row, rows, page_rows):
+    """[Hkv, rows, d] cache of one sequence, gathered from its pages."""
+    pages = torch.from_numpy(table_row[: -(-rows // page_rows)].astype(np.int64)).cuda()
+    x = pool[pages]                                   # [k, Hkv, page_rows, d]
+    return x.permute(1, 0, 2, 3).reshape(pool.shape[1], -1, pool.shape[3])[:, :rows].contiguous()
+
+
+def check_batch(lengths, T, Hq, Hkv, page_rows, seed, parent=None):
+    parent = parent if parent is not None else wl.kary_tree_parent(T, 3)
+    q, kp, vp, table_t, table = make_batch(lengths, T, Hq, Hkv, page_rows, seed)
+    say("paged B=%d T=%d Hq=%d Hkv=%d page=%d lengths=%s" % (len(lengths), T, Hq, Hkv, page_rows, lengths))
+    o, lse = tsw.tree_attn_verify_paged(q, kp, vp, table_t, lengths, parent)
+    torch.cuda.synchronize()
+    for b, n in enumerate(lengths):
+        k = contiguous(kp, table[b], n + T, page_rows)
+        v = contiguous(vp, table[b], n + T, page_rows)
+        o_ref, l_ref = oracle.tree_attn(wl.oracle_view(q[b]), wl.oracle_view(k), wl.oracle_view(v), parent, n,
+                                        1 / np.sqrt(128), nthreads=NTHREADS)
+        eo = float(np.max(np.abs(o[b].cpu().double().numpy() - o_ref)))
+        el = float(np.max(np.abs(lse[b].cpu().double().numpy() - l_ref)))
+        say("  seq %d n_prefix %d: max|dO| %.3g max|dLSE| %.3g" % (b, n, eo, el))
+        assert eo <= TOL and el <= TOL, (b, n, eo, el)
+
+
+def test_paged_single_sequence():
+    check_batch([5000], 40, 32, 8, 16, 1)
+
+
+def test_paged_mixed_lengths():
+    # a length on a page boundary, tree rows crossing a page, a short one
+    check_batch([4096, 3001, 777, 12000, 300], 40, 32, 8, 16, 2)
+
+
+def test_paged_large_pages_and_mha():
+    check_batch([2500, 6400], 13, 16, 16, 256, 3)
+
+
+def test_paged_gqa14b_shape():
+    check_batch([3333, 1500, 9000], 40, 40, 8, 64, 4)
+
+
+def test_paged_random_tree_T64():
+    check_batch([2000, 4500], 64, 8, 2, 32, 5, parent=wl.random_tree_parent(64, 5))
+
+
+def test_paged_many_sequences():
+    check_batch([400 + 137 * b for b in range(16)], 13, 32, 8, 16, 6)
+
+
+def test_paged_matches_contiguous_call():
+    """One sequence in pages vs the same cache contiguous: same definition,
+    two kernels; both within the tolerance of each other."""
+    T, Hq, Hkv = 40, 32, 8
+    parent = wl.kary_tree_parent(T, 3)
+    q, kp, vp, table_t, table = make_batch([20000], T, Hq, Hkv, 16, 7)
+    o, lse = tsw.tree_attn_verify_paged(q, kp, vp, table_t, [20000], parent)
+    k = contiguous(kp, table[0], 20000 + T, 16)
+    v = contiguous(vp, table[0], 20000 + T, 16)
+    o2, l2 = tsw.tree_attn_verify(q[0].contiguous(), k, v, parent, 20000)
+    torch.cuda.synchronize()
+    assert float((o[0] - o2).abs().max()) <= TOL and float((lse[0] - l2).abs().max()) <= TOL

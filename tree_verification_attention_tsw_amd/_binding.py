@@ -35,6 +35,14 @@ class AttnDesc(ctypes.Structure):
     ]
 
 
+class PagedDesc(ctypes.Structure):
+    _fields_ = [
+        ("B", ctypes.c_int32), ("T", ctypes.c_int32), ("Hq", ctypes.c_int32), ("Hkv", ctypes.c_int32),
+        ("d", ctypes.c_int32), ("page_rows", ctypes.c_int32), ("max_pages", ctypes.c_int32),
+        ("dtype", ctypes.c_int32), ("scale", ctypes.c_float), ("reserved", ctypes.c_int32),
+    ]
+
+
 _lib = None
 
 
@@ -57,6 +65,9 @@ def lib():
     L.tsw_tree_attn_partial.argtypes = [D, vp, vp, vp, vp, vp, i64, vp, vp, vp, sz, vp]
     L.tsw_tree_attn_split.argtypes = [D, vp, vp, vp, vp, vp, i64, i32, vp, vp, vp]
     L.tsw_lse_merge.argtypes = [i32, i64, i32, vp, vp, vp, vp, vp]
+    PD = ctypes.POINTER(PagedDesc)
+    L.tsw_paged_workspace_size.argtypes = [PD, vp, ctypes.POINTER(sz)]
+    L.tsw_tree_attn_verify_paged.argtypes = [PD, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.tsw_accept_workspace_size.argtypes = [i32, i64, ctypes.POINTER(sz)]
     L.tsw_accept_greedy.argtypes = [vp, i32, vp, i64, i32, vp, vp, vp, sz, vp]
     L.tsw_kv_compact.argtypes = [vp, vp, i32, i64, i32, i32, i32, i64, i64, i32, vp, vp]
@@ -65,7 +76,7 @@ def lib():
     for name in ("tsw_tree_mask_build", "tsw_plan_splits", "tsw_workspace_size",
                  "tsw_tree_attn_verify", "tsw_tree_attn_partial", "tsw_tree_attn_split",
                  "tsw_lse_merge", "tsw_accept_workspace_size", "tsw_accept_greedy",
-                 "tsw_kv_compact"):
+                 "tsw_kv_compact", "tsw_paged_workspace_size", "tsw_tree_attn_verify_paged"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L
@@ -388,3 +399,70 @@ def kv_compact(k, v, n_prefix, T, result):
 def prepare_compact(k, v, n_prefix, T, result, stream=None):
     return PreparedCall(lib().tsw_kv_compact, _compact_args(k, v, n_prefix, T, result, stream),
                         "tsw_kv_compact", (k, v, result))
+
+
+# ------------------------------------------------------------ paged batch
+
+def make_paged_desc(q, k_pages, block_table, scale=None):
+    """Descriptor for q [B, T, Hq, d], a page pool [n_pages, Hkv, page_rows, d]
+    and a block table [B, max_pages]."""
+    B, T, Hq, d = q.shape
+    _, Hkv, page_rows, d2 = k_pages.shape
+    if d2 != d or block_table.shape[0] != B:
+        raise ValueError("shape mismatch between q, pages and block table")
+    return PagedDesc(B=B, T=T, Hq=Hq, Hkv=Hkv, d=d, page_rows=page_rows,
+                     max_pages=block_table.shape[1],
+                     dtype=DTYPE_BF16 if q.dtype == torch.bfloat16 else DTYPE_F32,
+                     scale=float(scale) if scale is not None else 1.0 / float(np.sqrt(d)), reserved=0)
+
+
+def _paged_lengths(n_prefix):
+    return np.ascontiguousarray(np.asarray(n_prefix, dtype=np.int64))
+
+
+def paged_workspace_size(q, k_pages, block_table, n_prefix, scale=None):
+    desc = make_paged_desc(q, k_pages, block_table, scale)
+    npf = _paged_lengths(n_prefix)
+    n = ctypes.c_size_t(0)
+    _check(lib().tsw_paged_workspace_size(ctypes.byref(desc), _np_ptr(npf), ctypes.byref(n)),
+           "tsw_paged_workspace_size")
+    return n.value
+
+
+def _paged_args(q, k_pages, v_pages, block_table, n_prefix, parent, o, lse, workspace, scale, stream):
+    for t in (q, k_pages, v_pages):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError("q and the page pools must be contiguous GPU tensors")
+    if block_table.dtype != torch.int32 or not block_table.is_cuda or not block_table.is_contiguous():
+        raise ValueError("block_table must be a contiguous int32 GPU tensor")
+    desc = make_paged_desc(q, k_pages, block_table, scale)
+    npf = _paged_lengths(n_prefix)
+    p = _parent_arr(parent)
+    st = ctypes.c_void_p(stream.cuda_stream if stream is not None
+                         else torch.cuda.current_stream(q.device).cuda_stream)
+    args = (ctypes.byref(desc), _dev_ptr(q), _dev_ptr(k_pages), _dev_ptr(v_pages), _dev_ptr(block_table),
+            _np_ptr(npf), _np_ptr(p), _dev_ptr(o), _dev_ptr(lse), _dev_ptr(workspace), workspace.numel(), st)
+    return args, (desc, npf, p)
+
+
+def tree_attn_verify_paged(q, k_pages, v_pages, block_table, n_prefix, parent, scale=None, out=None,
+                           workspace=None):
+    """Paged batch verification; returns (o [B, T, Hq, d], lse [B, T, Hq])."""
+    B, T, Hq, d = q.shape
+    o, lse = out if out is not None else (
+        torch.empty((B, T, Hq, d), dtype=torch.float32, device=q.device),
+        torch.empty((B, T, Hq), dtype=torch.float32, device=q.device))
+    if workspace is None:
+        workspace = torch.empty(max(paged_workspace_size(q, k_pages, block_table, n_prefix, scale), 256),
+                                dtype=torch.uint8, device=q.device)
+    args, _keep = _paged_args(q, k_pages, v_pages, block_table, n_prefix, parent, o, lse, workspace, scale,
+                              None)
+    _check(lib().tsw_tree_attn_verify_paged(*args), "tsw_tree_attn_verify_paged")
+    return o, lse
+
+
+def prepare_verify_paged(q, k_pages, v_pages, block_table, n_prefix, parent, o, lse, workspace, scale=None,
+                         stream=None):
+    args, keep = _paged_args(q, k_pages, v_pages, block_table, n_prefix, parent, o, lse, workspace, scale,
+                             stream)
+    return PreparedCall(lib().tsw_tree_attn_verify_paged, args, "tsw_tree_attn_verify_paged", keep)

@@ -163,6 +163,7 @@ int run_split(const tsw_attn_desc* d, const void* q, const void* k, const void* 
     a.M = a.T * a.G;
     a.n_splits = n_splits;
     a.scale_log2 = d->scale * kLog2e;
+    a.B = 1;
 
     tsw::MfmaConfig cfg;
     if (use_mfma(d, n_keys, &cfg)) {
@@ -171,7 +172,8 @@ int run_split(const tsw_attn_desc* d, const void* q, const void* k, const void* 
         if (gather && a.chunk_keys > tsw::kGatherChunkMax) return TSW_EUNSUPPORTED;
         if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v) & 15) return TSW_EINVAL;
         if (d->kv_head_stride % 8) return TSW_EINVAL;
-        return hip_status(tsw::launch_split_mfma(cfg, gather, a, d->Hkv, stream));
+        return hip_status(tsw::launch_split_mfma(cfg, gather ? tsw::kModeGather : tsw::kModeContig, a, d->Hkv,
+                                                 stream));
     }
     a.chunk_keys = cdiv(cdiv(n_keys, n_splits), tsw::kValuTile) * tsw::kValuTile;
     return hip_status(tsw::launch_split_valu(d->dtype, d->d, gather, a, d->Hkv, stream));
@@ -235,6 +237,52 @@ int check_accept_shape(int32_t T, int64_t vocab) {
     if (T < 1 || T > kMaxNodes) return TSW_EINVAL;
     if (vocab < 1 || vocab > INT32_MAX) return TSW_EINVAL;
     return TSW_OK;
+}
+
+// Paged batch: per-split page-table slices live in the 4096-entry LDS
+// buffer the gather variant uses for index slices (a few entries are kept
+// for the tree rows' pages).
+constexpr int64_t kPagedSlicePages = 4080;
+
+int check_paged(const tsw_paged_desc* d, const int64_t* n_prefix, int64_t* n_max, tsw::MfmaConfig* cfg) {
+    if (!d || !n_prefix) return TSW_EINVAL;
+    if (d->reserved != 0) return TSW_EINVAL;
+    if (d->B < 1 || d->B > 64 || d->T < 1 || d->T > kMaxNodes) return TSW_EINVAL;
+    if (d->Hq < 1 || d->Hkv < 1 || d->Hq % d->Hkv != 0) return TSW_EINVAL;
+    if (!(d->scale > 0.0f) || !isfinite(d->scale)) return TSW_EINVAL;
+    if (d->d != 128 || d->dtype != TSW_DTYPE_BF16) return TSW_EUNSUPPORTED;
+    if (d->page_rows < 16 || d->page_rows > 4096 || (d->page_rows & (d->page_rows - 1))) return TSW_EINVAL;
+    if (!tsw::mfma_config_for(d->T * (d->Hq / d->Hkv), cfg)) return TSW_EUNSUPPORTED;
+    *n_max = 0;
+    for (int b = 0; b < d->B; ++b) {
+        if (n_prefix[b] < 0) return TSW_EINVAL;
+        if (cdiv(n_prefix[b] + d->T, d->page_rows) > d->max_pages) return TSW_EINVAL;
+        if (n_prefix[b] > *n_max) *n_max = n_prefix[b];
+    }
+    return TSW_OK;
+}
+
+int plan_paged(const tsw_paged_desc* d, int64_t n_max, const tsw::MfmaConfig& cfg, int32_t* n_splits) {
+    int cus = 0;
+    int rc = device_cus(&cus);
+    if (rc != TSW_OK) return rc;
+    const int64_t tk = cfg.tile_keys();
+    int64_t s = cus / ((int64_t)d->Hkv * d->B);
+    if (s < 1) s = 1;
+    const int64_t by_len = cdiv(n_max, 2 * tk);
+    if (s > by_len) s = by_len;
+    const int64_t need = cdiv(n_max, kPagedSlicePages * d->page_rows);
+    if (s < need) s = need;
+    if (s < 1) s = 1;
+    if (s > 65535) return TSW_EUNSUPPORTED;
+    *n_splits = (int32_t)s;
+    return TSW_OK;
+}
+
+size_t ws_bytes_paged(const tsw_paged_desc* d, int32_t n_splits) {
+    const size_t rows = (size_t)d->B * d->T * d->Hq;
+    return align256((size_t)n_splits * rows * d->d * sizeof(float)) +
+           align256((size_t)n_splits * rows * sizeof(float));
 }
 
 }  // namespace
@@ -361,6 +409,66 @@ int tsw_kv_compact(void* k, void* v, int32_t n_layers, int64_t layer_stride, int
     a.esz = esz;
     a.row_bytes = d * esz;
     return hip_status(tsw::launch_kv_compact(a, n_layers, Hkv, result, (hipStream_t)stream));
+}
+
+int tsw_paged_workspace_size(const tsw_paged_desc* desc, const int64_t* n_prefix, size_t* bytes) {
+    if (!bytes) return TSW_EINVAL;
+    int64_t n_max = 0;
+    tsw::MfmaConfig cfg;
+    int rc = check_paged(desc, n_prefix, &n_max, &cfg);
+    if (rc != TSW_OK) return rc;
+    int32_t s = 0;
+    rc = plan_paged(desc, n_max, cfg, &s);
+    if (rc != TSW_OK) return rc;
+    *bytes = ws_bytes_paged(desc, s);
+    return TSW_OK;
+}
+
+int tsw_tree_attn_verify_paged(const tsw_paged_desc* desc, const void* q, const void* k_pages, const void* v_pages,
+                               const int32_t* block_table, const int64_t* n_prefix, const int32_t* parent, float* o,
+                               float* lse, void* workspace, size_t workspace_bytes, tsw_stream_t stream) {
+    int64_t n_max = 0;
+    tsw::MfmaConfig cfg;
+    int rc = check_paged(desc, n_prefix, &n_max, &cfg);
+    if (rc != TSW_OK) return rc;
+    if (!q || !k_pages || !v_pages || !block_table || !parent || !o || !lse || !workspace) return TSW_EINVAL;
+    if (((uintptr_t)q | (uintptr_t)k_pages | (uintptr_t)v_pages) & 15) return TSW_EINVAL;
+    if ((uintptr_t)workspace & 255) return TSW_EINVAL;
+    SplitArgs a;
+    memset(&a, 0, sizeof a);
+    rc = build_mask(parent, desc->T, a.mask, nullptr);
+    if (rc != TSW_OK) return rc;
+    int32_t n_splits = 0;
+    rc = plan_paged(desc, n_max, cfg, &n_splits);
+    if (rc != TSW_OK) return rc;
+    if (workspace_bytes < ws_bytes_paged(desc, n_splits)) return TSW_ENOSPACE;
+    const size_t rows = (size_t)desc->B * desc->T * desc->Hq;
+    float* part_o = (float*)workspace;
+    float* part_lse = (float*)((char*)workspace + align256((size_t)n_splits * rows * desc->d * sizeof(float)));
+    a.q = q;
+    a.k = k_pages;
+    a.v = v_pages;
+    a.part_o = part_o;
+    a.part_lse = part_lse;
+    a.T = desc->T;
+    a.Hq = desc->Hq;
+    a.Hkv = desc->Hkv;
+    a.G = desc->Hq / desc->Hkv;
+    a.M = a.T * a.G;
+    a.n_splits = n_splits;
+    a.scale_log2 = desc->scale * kLog2e;
+    a.B = desc->B;
+    a.table = block_table;
+    a.table_stride = desc->max_pages;
+    a.page_rows = desc->page_rows;
+    int shift = 0;
+    while ((1 << shift) < desc->page_rows) ++shift;
+    a.page_shift = shift;
+    for (int b = 0; b < desc->B; ++b) a.npb[b] = n_prefix[b];
+    rc = hip_status(tsw::launch_split_mfma(cfg, tsw::kModePaged, a, desc->Hkv, (hipStream_t)stream));
+    if (rc != TSW_OK) return rc;
+    return hip_status(tsw::launch_lse_merge(n_splits, (int64_t)rows, desc->d, part_o, part_lse, o, lse,
+                                            (hipStream_t)stream));
 }
 
 const char* tsw_status_str(int status) {

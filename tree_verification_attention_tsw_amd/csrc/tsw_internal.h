@@ -8,6 +8,11 @@
 
 namespace tsw {
 
+// How the split kernels find a key's K/V row: the cache position itself
+// (contiguous), through an index list (gather, the draft pass), or through
+// a per-sequence block table into a page pool (paged batch).
+enum { kModeContig = 0, kModeGather = 1, kModePaged = 2 };
+
 // Everything a split kernel needs, passed by value as the kernel argument.
 // The tree mask travels here (one 64-bit word per node) so that no device
 // buffer or host-to-device copy is needed for it.
@@ -24,8 +29,13 @@ struct SplitArgs {
     int64_t chunk_keys;      // prefix keys per split, a multiple of the kernel's key tile
     int32_t T, Hq, Hkv, G, M, n_splits;
     float scale_log2;        // scale * log2(e): scores are exponentiated base 2
-    int32_t pad_;
+    int32_t B;               // sequences (grid z); 1 unless paged
     uint64_t mask[64];       // ancestor-or-self bits per node
+    // paged batch: k/v point at page pools [n_pages][Hkv][page_rows][d];
+    // sequence b's logical page j is table[b * table_stride + j]
+    const int32_t* table;
+    int32_t table_stride, page_rows, page_shift, pad_;
+    int64_t npb[64];         // committed length per sequence
 };
 
 // Matrix-core kernel shapes.  A work-group holds `waves` wavefronts: `rgroups`
@@ -43,7 +53,7 @@ constexpr int kGatherChunkMax = 4096;
 // when no shape covers M (callers then use the vector-ALU kernel).
 bool mfma_config_for(int M, MfmaConfig* cfg);
 
-hipError_t launch_split_mfma(const MfmaConfig& cfg, bool gather, const SplitArgs& a,
+hipError_t launch_split_mfma(const MfmaConfig& cfg, int mode, const SplitArgs& a,
                              int n_kv_heads, hipStream_t stream);
 hipError_t launch_split_valu(int dtype, int d, bool gather, const SplitArgs& a, int n_kv_heads,
                              hipStream_t stream);

@@ -8,7 +8,7 @@ namespace tsw {
     X(4, 1, 1) X(4, 1, 2) X(4, 1, 3) X(4, 1, 4) X(4, 2, 3) X(4, 2, 4) X(4, 2, 5) X(4, 4, 3) X(4, 4, 4) \
     X(4, 4, 5) X(8, 2, 2) X(8, 4, 2) X(8, 4, 3) X(8, 8, 2) X(8, 8, 3)
 #define TSW_DECLARE(w, r, nb) \
-    hipError_t launch_mfma_##w##_##r##_##nb(bool gather, const SplitArgs& a, int n_kv_heads, hipStream_t stream);
+    hipError_t launch_mfma_##w##_##r##_##nb(int mode, const SplitArgs& a, int n_kv_heads, hipStream_t stream);
 TSW_SHAPES(TSW_DECLARE)
 
 bool mfma_config_for(int M, MfmaConfig* cfg) {
@@ -29,11 +29,11 @@ bool mfma_config_for(int M, MfmaConfig* cfg) {
     return true;
 }
 
-hipError_t launch_split_mfma(const MfmaConfig& cfg, bool gather, const SplitArgs& a, int n_kv_heads,
+hipError_t launch_split_mfma(const MfmaConfig& cfg, int mode, const SplitArgs& a, int n_kv_heads,
                              hipStream_t stream) {
 #define TSW_CASE(W_, R_, NB_)                                  \
     if (cfg.waves == W_ && cfg.rgroups == R_ && cfg.nb == NB_) \
-        return launch_mfma_##W_##_##R_##_##NB_(gather, a, n_kv_heads, stream);
+        return launch_mfma_##W_##_##R_##_##NB_(mode, a, n_kv_heads, stream);
     TSW_SHAPES(TSW_CASE)
 #undef TSW_CASE
     return hipErrorInvalidValue;

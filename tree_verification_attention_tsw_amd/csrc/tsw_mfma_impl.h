@@ -50,7 +50,7 @@ namespace mfma {
 // (logits far below zero) and precision could suffer; rerun exactly.
 constexpr float kMinRowSum = 0x1p-60f;
 
-template <int W_, int R_, int NB_, bool GATHER_>
+template <int W_, int R_, int NB_, int MODE_>
 struct Shape {
     static constexpr int R = R_;
     static constexpr int NB = NB_;
@@ -61,10 +61,10 @@ struct Shape {
     static constexpr int STAGE = 2 * TK * ROWB;     // one K tile + one V tile
     static constexpr int NI = TK / (2 * WAVES);     // DMA instructions per wave per tile
     // LDS beyond the ring: row-sum pool and votes, the tree mask, and for
-    // the gather variant the staged index slice.
+    // the gather and paged variants the staged index or page-table slice.
     static constexpr int POOL = WAVES * NB * 16 * 4 + WAVES * 4;
     static constexpr int MASK_BYTES = 64 * 8;
-    static constexpr int IDX_BYTES = GATHER_ ? kGatherChunkMax * 4 : 0;
+    static constexpr int IDX_BYTES = MODE_ != kModeContig ? kGatherChunkMax * 4 : 0;
     static constexpr int RESERVE = ((POOL + MASK_BYTES + 255) & ~255) + IDX_BYTES;
     // as many stages as the LDS holds (up to 16): more tiles in flight
     static constexpr int STAGES_FIT = (160 * 1024 - RESERVE) / STAGE;
@@ -81,11 +81,16 @@ struct Shape {
 
 struct Ctx {
     char* smem;
-    const int32_t* idx_lds;
+    const int32_t* idx_lds;      // gather: index slice; paged: page-table slices
     const uint64_t* mask_lds;    // the tree mask, copied to LDS
-    const char* kbase;
+    const char* kbase;           // this kv head's cache (paged: the page pool)
     const char* vbase;
+    const __bf16* q;             // this sequence's queries
+    int64_t n_prefix;            // this sequence's committed length
     int64_t c0, c1;      // prefix key range [c0, c1) of this split
+    int64_t pg0, tpg0;   // paged: first page of the slice and of the tree rows
+    int64_t row0;        // partial-output row of (split, sequence, node 0)
+    int npg;             // paged: pages staged for the slice
     int n_pre_tiles, n_tiles;
     int lane, li, lj, w, rg, ks, split, g;
 };
@@ -94,12 +99,12 @@ struct Ctx {
 // four 256-byte rows (64 lanes x 16 bytes) into consecutive LDS; lane (li,
 // lj) of instruction i writes logical chunk li ^ swz(row) of its row.  Rows
 // past the slice end re-read a valid row (their scores are masked to -inf).
-template <class S, bool GATHER>
+template <class S, int MODE>
 __device__ __forceinline__ void issue_tile(const SplitArgs& a, const Ctx& cx, int tt, int st) {
     char* sbase = cx.smem + st * S::STAGE;
     const bool pre = tt < cx.n_pre_tiles;
     const int64_t k0 = cx.c0 + (int64_t)tt * S::TK;
-    if (!GATHER && pre && k0 + S::TK <= cx.c1) {
+    if (MODE == kModeContig && pre && k0 + S::TK <= cx.c1) {
         // Whole tile of consecutive cache rows: a uniform base per tile and a
         // fixed 32-bit offset per lane and instruction.
         const char* kt = cx.kbase + k0 * S::ROWB;
@@ -127,11 +132,17 @@ __device__ __forceinline__ void issue_tile(const SplitArgs& a, const Ctx& cx, in
         if (pre) {
             int64_t kk = k0 + row;
             if (kk >= cx.c1) kk = cx.c0;
-            pos = GATHER ? (int64_t)cx.idx_lds[kk - cx.c0] : kk;
+            pos = MODE == kModeGather ? (int64_t)cx.idx_lds[kk - cx.c0] : kk;
         } else {
             int jj = (tt - cx.n_pre_tiles) * S::TK + row;
             if (jj >= a.T) jj = a.T - 1;
-            pos = a.n_prefix + jj;
+            pos = cx.n_prefix + jj;
+        }
+        if constexpr (MODE == kModePaged) {
+            // sequence position -> (page from the staged table, row in page)
+            const int64_t lp = pos >> a.page_shift;
+            const int slot = pre ? (int)(lp - cx.pg0) : cx.npg + (int)(lp - cx.tpg0);
+            pos = ((int64_t)cx.idx_lds[slot] * a.Hkv + cx.g) * a.page_rows + (pos & (a.page_rows - 1));
         }
         const char* src = (isv ? cx.vbase : cx.kbase) + pos * S::ROWB + 16 * (cx.li ^ swz(row));
         char* dst = sbase + (isv ? S::TK * S::ROWB : 0) + grp * 1024;
@@ -344,7 +355,7 @@ __device__ __forceinline__ void tile_max(const SplitArgs& a, const Ctx& cx, int 
 }
 
 // The work of one wavefront owning NBA query blocks.
-template <class S, bool GATHER, int NBA>
+template <class S, int LAYOUT, int NBA>
 __device__ __forceinline__ void run_wave(const SplitArgs& a, const Ctx& cx) {
     constexpr int STAGES = S::STAGES;
     const float c = a.scale_log2;
@@ -360,7 +371,7 @@ __device__ __forceinline__ void run_wave(const SplitArgs& a, const Ctx& cx) {
         const bool ok = r < a.M;
         const int t = ok ? r / a.G : 0;
         const int h = cx.g * a.G + (ok ? r % a.G : 0);
-        const bf16x8* src = (const bf16x8*)((const __bf16*)a.q + ((size_t)t * a.Hq + h) * 128 + 8 * cx.lj);
+        const bf16x8* src = (const bf16x8*)(cx.q + ((size_t)t * a.Hq + h) * 128 + 8 * cx.lj);
 #pragma unroll
         for (int s = 0; s < 4; ++s) qop[b][s] = src[4 * s];
     }
@@ -369,12 +380,12 @@ __device__ __forceinline__ void run_wave(const SplitArgs& a, const Ctx& cx) {
     // hides under the first tile's and the tile loop never waits on Q.
     if (n >= STAGES - 1) {
 #pragma unroll
-        for (int s = 0; s < STAGES - 1; ++s) issue_tile<S, GATHER>(a, cx, s, s);
+        for (int s = 0; s < STAGES - 1; ++s) issue_tile<S, LAYOUT>(a, cx, s, s);
         wait_vmcnt<(STAGES - 1) * S::NI>();
     } else {
 #pragma unroll
         for (int s = 0; s < STAGES - 1; ++s)
-            if (s < n) issue_tile<S, GATHER>(a, cx, s, s);
+            if (s < n) issue_tile<S, LAYOUT>(a, cx, s, s);
         wait_vmcnt<0>();
     }
 
@@ -402,7 +413,7 @@ __device__ __forceinline__ void run_wave(const SplitArgs& a, const Ctx& cx) {
             barrier_lds();
 #pragma unroll
             for (int s = 0; s < STAGES - 1; ++s)
-                if (s < n) issue_tile<S, GATHER>(a, cx, s, s);
+                if (s < n) issue_tile<S, LAYOUT>(a, cx, s, s);
         }
         // Full prefix tiles come first; the ragged end of the slice and the
         // tree's own rows (masked) come last, so the two kinds run in two
@@ -415,7 +426,7 @@ __device__ __forceinline__ void run_wave(const SplitArgs& a, const Ctx& cx) {
             wait_tile<S>(newer);
             barrier_lds();
             // The stage of tile t-1 is free once every wave passed the barrier.
-            if (t + STAGES - 1 < n) issue_tile<S, GATHER>(a, cx, t + STAGES - 1, (t + STAGES - 1) % STAGES);
+            if (t + STAGES - 1 < n) issue_tile<S, LAYOUT>(a, cx, t + STAGES - 1, (t + STAGES - 1) % STAGES);
             const char* Ks = cx.smem + (t % STAGES) * S::STAGE;
             if constexpr (MODE == MAXONLY) {
                 load_k<S>(Ks, cx, kop);
@@ -537,7 +548,7 @@ __device__ __forceinline__ void run_wave(const SplitArgs& a, const Ctx& cx) {
         const int rbase = (cx.rg + b * S::R) * 16;
         if (cx.lj == 0 && rbase + cx.li < a.M) {
             const int r = rbase + cx.li;
-            const size_t orow = ((size_t)cx.split * a.T + r / a.G) * a.Hq + cx.g * a.G + r % a.G;
+            const size_t orow = ((size_t)cx.row0 + r / a.G) * a.Hq + cx.g * a.G + r % a.G;
             a.part_lse[orow] = L > 0.0f ? (mmax + __log2f(L)) * kLn2 : -INFINITY;
         }
         // accumulator element i of this lane belongs to row 4*lj + i; the
@@ -555,7 +566,7 @@ __device__ __forceinline__ void run_wave(const SplitArgs& a, const Ctx& cx) {
             const int r = rbase + q;
             row_ok[i] = r < a.M;
             const int rr = row_ok[i] ? r : rbase;
-            const size_t orow = ((size_t)cx.split * a.T + rr / a.G) * a.Hq + cx.g * a.G + rr % a.G;
+            const size_t orow = ((size_t)cx.row0 + rr / a.G) * a.Hq + cx.g * a.G + rr % a.G;
             dst[i] = a.part_o + orow * 128 + cx.li;
         }
 #pragma unroll
@@ -576,9 +587,9 @@ __device__ __forceinline__ void run_wave(const SplitArgs& a, const Ctx& cx) {
     }
 }
 
-template <int W, int R, int NB, bool GATHER>
+template <int W, int R, int NB, int MODE>
 __global__ __launch_bounds__(W * 64, 1) void split_mfma(const SplitArgs a) {
-    using S = Shape<W, R, NB, GATHER>;
+    using S = Shape<W, R, NB, MODE>;
     constexpr int SMEM = S::SMEM;
     constexpr int MASK_OFF = (SMEM + S::POOL + 7) & ~7;
     static_assert(MASK_OFF + 64 * 8 <= 160 * 1024, "LDS budget");
@@ -600,22 +611,51 @@ __global__ __launch_bounds__(W * 64, 1) void split_mfma(const SplitArgs a) {
     cx.ks = cx.w % S::KS;
     cx.split = blockIdx.x;
     cx.g = blockIdx.y;
-    cx.c0 = (int64_t)cx.split * a.chunk_keys;
-    cx.c1 = cx.c0 + a.chunk_keys < a.n_keys ? cx.c0 + a.chunk_keys : a.n_keys;
+    const int b = blockIdx.z;                       // sequence of a paged batch (else 0)
+    int64_t n_keys = a.n_keys, chunk = a.chunk_keys;
+    cx.n_prefix = a.n_prefix;
+    if constexpr (MODE == kModePaged) {
+        cx.n_prefix = a.npb[b];
+        n_keys = cx.n_prefix;
+        chunk = (n_keys + a.n_splits - 1) / a.n_splits;
+        chunk = (chunk + S::TK - 1) / S::TK * S::TK;
+    }
+    cx.q = (const __bf16*)a.q + (size_t)b * a.T * a.Hq * 128;
+    cx.row0 = ((int64_t)cx.split * a.B + b) * a.T;
+    cx.c0 = (int64_t)cx.split * chunk;
+    if (cx.c0 > n_keys) cx.c0 = n_keys;
+    cx.c1 = cx.c0 + chunk < n_keys ? cx.c0 + chunk : n_keys;
     cx.n_pre_tiles = cx.c1 > cx.c0 ? (int)((cx.c1 - cx.c0 + S::TK - 1) / S::TK) : 0;
     const int n_tail_tiles = cx.split == a.n_splits - 1 ? (a.T + S::TK - 1) / S::TK : 0;
     cx.n_tiles = cx.n_pre_tiles + n_tail_tiles;
-    cx.kbase = (const char*)a.k + (size_t)cx.g * (size_t)a.kv_head_stride * 2;
-    cx.vbase = (const char*)a.v + (size_t)cx.g * (size_t)a.kv_head_stride * 2;
+    // paged caches fold the head into the page row; others offset by head
+    const size_t head_off = MODE == kModePaged ? 0 : (size_t)cx.g * (size_t)a.kv_head_stride * 2;
+    cx.kbase = (const char*)a.k + head_off;
+    cx.vbase = (const char*)a.v + head_off;
     int32_t* idx_lds = (int32_t*)(smem + S::RING);
     cx.idx_lds = idx_lds;
     uint64_t* mask_lds = (uint64_t*)(smem + MASK_OFF);
     cx.mask_lds = mask_lds;
     // visible to all waves after the first barrier of the tile loop
     if (threadIdx.x < (unsigned)a.T) mask_lds[threadIdx.x] = a.mask[threadIdx.x];
-    if constexpr (GATHER) {
+    cx.pg0 = cx.tpg0 = 0;
+    cx.npg = 0;
+    if constexpr (MODE == kModeGather) {
         const int n = (int)(cx.c1 > cx.c0 ? cx.c1 - cx.c0 : 0);
         for (int i = threadIdx.x; i < n; i += S::WAVES * 64) idx_lds[i] = a.idx[cx.c0 + i];
+        __syncthreads();
+    }
+    if constexpr (MODE == kModePaged) {
+        // the pages of this split's slice, then (last split) those of the
+        // tree rows, from this sequence's row of the block table
+        const int32_t* table = a.table + (size_t)b * a.table_stride;
+        cx.pg0 = cx.c0 >> a.page_shift;
+        cx.npg = cx.c1 > cx.c0 ? (int)(((cx.c1 - 1) >> a.page_shift) - cx.pg0 + 1) : 0;
+        cx.tpg0 = cx.n_prefix >> a.page_shift;
+        const int ntp = cx.split == a.n_splits - 1
+                            ? (int)(((cx.n_prefix + a.T - 1) >> a.page_shift) - cx.tpg0 + 1) : 0;
+        for (int i = threadIdx.x; i < cx.npg; i += S::WAVES * 64) idx_lds[i] = table[cx.pg0 + i];
+        for (int i = threadIdx.x; i < ntp; i += S::WAVES * 64) idx_lds[cx.npg + i] = table[cx.tpg0 + i];
         __syncthreads();
     }
 
@@ -624,18 +664,22 @@ __global__ __launch_bounds__(W * 64, 1) void split_mfma(const SplitArgs a) {
     const int nblk = (a.M + 15) >> 4;
     const int nb_act = (nblk - cx.rg + S::R - 1) / S::R;
     if constexpr (S::R == 1) {
-        run_wave<S, GATHER, NB>(a, cx);
+        run_wave<S, MODE, NB>(a, cx);
     } else {
-        if (nb_act >= NB) run_wave<S, GATHER, NB>(a, cx);
-        else run_wave<S, GATHER, NB - 1>(a, cx);
+        if (nb_act >= NB) run_wave<S, MODE, NB>(a, cx);
+        else run_wave<S, MODE, NB - 1>(a, cx);
     }
 }
 
 template <int W, int R, int NB>
-hipError_t launch(bool gather, const SplitArgs& a, int n_kv_heads, hipStream_t stream) {
-    const dim3 grid(a.n_splits, n_kv_heads);
-    if (gather) hipLaunchKernelGGL((split_mfma<W, R, NB, true>), grid, dim3(W * 64), 0, stream, a);
-    else hipLaunchKernelGGL((split_mfma<W, R, NB, false>), grid, dim3(W * 64), 0, stream, a);
+hipError_t launch(int mode, const SplitArgs& a, int n_kv_heads, hipStream_t stream) {
+    const dim3 grid(a.n_splits, n_kv_heads, a.B);
+    if (mode == kModeGather)
+        hipLaunchKernelGGL((split_mfma<W, R, NB, kModeGather>), grid, dim3(W * 64), 0, stream, a);
+    else if (mode == kModePaged)
+        hipLaunchKernelGGL((split_mfma<W, R, NB, kModePaged>), grid, dim3(W * 64), 0, stream, a);
+    else
+        hipLaunchKernelGGL((split_mfma<W, R, NB, kModeContig>), grid, dim3(W * 64), 0, stream, a);
     return hipGetLastError();
 }
 

@@ -13,8 +13,8 @@
 
 namespace tsw {
 
-hipError_t TSW_LAUNCH_NAME(TSW_W, TSW_R, TSW_NB)(bool gather, const SplitArgs& a, int n_kv_heads, hipStream_t stream) {
-    return mfma::launch<TSW_W, TSW_R, TSW_NB>(gather, a, n_kv_heads, stream);
+hipError_t TSW_LAUNCH_NAME(TSW_W, TSW_R, TSW_NB)(int mode, const SplitArgs& a, int n_kv_heads, hipStream_t stream) {
+    return mfma::launch<TSW_W, TSW_R, TSW_NB>(mode, a, n_kv_heads, stream);
 }
 
 }  // namespace tsw
