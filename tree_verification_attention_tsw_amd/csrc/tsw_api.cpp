@@ -262,27 +262,53 @@ int check_paged(const tsw_paged_desc* d, const int64_t* n_prefix, int64_t* n_max
     return TSW_OK;
 }
 
-int plan_paged(const tsw_paged_desc* d, int64_t n_max, const tsw::MfmaConfig& cfg, int32_t* n_splits) {
+// Paged split plan: about one work-group per CU and kv head for the whole
+// batch, dealt so that the longest per-split slice (in key tiles) is as short
+// as possible; sequence b gets seg_base[b+1] - seg_base[b] splits (at least
+// one) of ceil(n_prefix[b] / splits) keys rounded up to whole tiles, and its
+// slices' pages must fit the LDS table.
+int plan_paged(const tsw_paged_desc* d, const int64_t* n_prefix, const tsw::MfmaConfig& cfg, int32_t* seg_base) {
     int cus = 0;
     int rc = device_cus(&cus);
     if (rc != TSW_OK) return rc;
     const int64_t tk = cfg.tile_keys();
-    int64_t s = cus / ((int64_t)d->Hkv * d->B);
-    if (s < 1) s = 1;
-    const int64_t by_len = cdiv(n_max, 2 * tk);
-    if (s > by_len) s = by_len;
-    const int64_t need = cdiv(n_max, kPagedSlicePages * d->page_rows);
-    if (s < need) s = need;
-    if (s < 1) s = 1;
-    if (s > 65535) return TSW_EUNSUPPORTED;
-    *n_splits = (int32_t)s;
+    int64_t target = cus / d->Hkv;
+    if (target < d->B) target = d->B;
+    const int64_t max_tiles = kPagedSlicePages * d->page_rows / tk;
+    // splits sequence b needs so that none of its slices exceeds `tiles`
+    auto splits_for = [&](int64_t b, int64_t tiles) {
+        const int64_t nt = cdiv(n_prefix[b], tk);
+        const int64_t sb = cdiv(nt, tiles);
+        return sb < 1 ? (int64_t)1 : sb;
+    };
+    auto total_for = [&](int64_t tiles) {
+        int64_t n = 0;
+        for (int b = 0; b < d->B; ++b) n += splits_for(b, tiles);
+        return n;
+    };
+    // smallest per-split tile count whose split total fits the target
+    int64_t lo = 2, hi = 2;
+    for (int b = 0; b < d->B; ++b) hi = cdiv(n_prefix[b], tk) > hi ? cdiv(n_prefix[b], tk) : hi;
+    while (lo < hi) {
+        const int64_t mid = (lo + hi) / 2;
+        if (total_for(mid) <= target) hi = mid;
+        else lo = mid + 1;
+    }
+    if (lo > max_tiles) lo = max_tiles;
+    seg_base[0] = 0;
+    for (int b = 0; b < d->B; ++b) {
+        const int64_t sb = splits_for(b, lo);
+        if (seg_base[b] + sb > 65535) return TSW_EUNSUPPORTED;
+        seg_base[b + 1] = (int32_t)(seg_base[b] + sb);
+    }
     return TSW_OK;
 }
 
-size_t ws_bytes_paged(const tsw_paged_desc* d, int32_t n_splits) {
-    const size_t rows = (size_t)d->B * d->T * d->Hq;
-    return align256((size_t)n_splits * rows * d->d * sizeof(float)) +
-           align256((size_t)n_splits * rows * sizeof(float));
+// Partials of a paged call: every split holds its own sequence's T x Hq rows.
+size_t ws_bytes_paged(const tsw_paged_desc* d, int32_t total_splits) {
+    const size_t rows = (size_t)d->T * d->Hq;
+    return align256((size_t)total_splits * rows * d->d * sizeof(float)) +
+           align256((size_t)total_splits * rows * sizeof(float));
 }
 
 }  // namespace
@@ -417,10 +443,10 @@ int tsw_paged_workspace_size(const tsw_paged_desc* desc, const int64_t* n_prefix
     tsw::MfmaConfig cfg;
     int rc = check_paged(desc, n_prefix, &n_max, &cfg);
     if (rc != TSW_OK) return rc;
-    int32_t s = 0;
-    rc = plan_paged(desc, n_max, cfg, &s);
+    int32_t seg_base[65];
+    rc = plan_paged(desc, n_prefix, cfg, seg_base);
     if (rc != TSW_OK) return rc;
-    *bytes = ws_bytes_paged(desc, s);
+    *bytes = ws_bytes_paged(desc, seg_base[desc->B]);
     return TSW_OK;
 }
 
@@ -438,13 +464,14 @@ int tsw_tree_attn_verify_paged(const tsw_paged_desc* desc, const void* q, const 
     memset(&a, 0, sizeof a);
     rc = build_mask(parent, desc->T, a.mask, nullptr);
     if (rc != TSW_OK) return rc;
-    int32_t n_splits = 0;
-    rc = plan_paged(desc, n_max, cfg, &n_splits);
+    rc = plan_paged(desc, n_prefix, cfg, a.seg_base);
     if (rc != TSW_OK) return rc;
+    const int32_t n_splits = a.seg_base[desc->B];
     if (workspace_bytes < ws_bytes_paged(desc, n_splits)) return TSW_ENOSPACE;
-    const size_t rows = (size_t)desc->B * desc->T * desc->Hq;
+    const size_t rows_per_seq = (size_t)desc->T * desc->Hq;
     float* part_o = (float*)workspace;
-    float* part_lse = (float*)((char*)workspace + align256((size_t)n_splits * rows * desc->d * sizeof(float)));
+    float* part_lse =
+        (float*)((char*)workspace + align256((size_t)n_splits * rows_per_seq * desc->d * sizeof(float)));
     a.q = q;
     a.k = k_pages;
     a.v = v_pages;
@@ -464,11 +491,17 @@ int tsw_tree_attn_verify_paged(const tsw_paged_desc* desc, const void* q, const 
     int shift = 0;
     while ((1 << shift) < desc->page_rows) ++shift;
     a.page_shift = shift;
+    a.page_bytes = (int64_t)desc->Hkv * desc->page_rows * desc->d * 2;
     for (int b = 0; b < desc->B; ++b) a.npb[b] = n_prefix[b];
     rc = hip_status(tsw::launch_split_mfma(cfg, tsw::kModePaged, a, desc->Hkv, (hipStream_t)stream));
     if (rc != TSW_OK) return rc;
-    return hip_status(tsw::launch_lse_merge(n_splits, (int64_t)rows, desc->d, part_o, part_lse, o, lse,
-                                            (hipStream_t)stream));
+    tsw::MergeSegs segs;
+    memset(&segs, 0, sizeof segs);
+    segs.n_seg = desc->B;
+    segs.rows_per_seg = (int64_t)rows_per_seq;
+    for (int b = 0; b <= desc->B; ++b) segs.base[b] = a.seg_base[b];
+    return hip_status(tsw::launch_lse_merge_segs(segs, (int64_t)rows_per_seq * desc->B, part_o, part_lse, o, lse,
+                                                 (hipStream_t)stream));
 }
 
 const char* tsw_status_str(int status) {

@@ -35,7 +35,21 @@ struct SplitArgs {
     // sequence b's logical page j is table[b * table_stride + j]
     const int32_t* table;
     int32_t table_stride, page_rows, page_shift, pad_;
+    int64_t page_bytes;      // Hkv * page_rows * d * 2: one page of the pool
     int64_t npb[64];         // committed length per sequence
+    // splits of sequence b are grid x in [seg_base[b], seg_base[b+1]), each
+    // ceil(n / splits) keys rounded up to whole tiles, but the last
+    int32_t seg_base[65];
+};
+
+// Partial rows grouped by sequence for the merge: sequence s owns splits
+// [base[s], base[s+1]), each split holding rows_per_seg rows.  A single
+// sequence has base = {0, n_splits}, rows_per_seg = all rows.
+struct MergeSegs {
+    int32_t n_seg;
+    int32_t pad_;
+    int64_t rows_per_seg;
+    int32_t base[65];
 };
 
 // Matrix-core kernel shapes.  A work-group holds `waves` wavefronts: `rgroups`
@@ -59,6 +73,8 @@ hipError_t launch_split_valu(int dtype, int d, bool gather, const SplitArgs& a, 
                              hipStream_t stream);
 hipError_t launch_lse_merge(int n_splits, int64_t n_rows, int d, const float* part_o,
                             const float* part_lse, float* o, float* lse, hipStream_t stream);
+hipError_t launch_lse_merge_segs(const MergeSegs& segs, int64_t n_rows, const float* part_o,
+                                 const float* part_lse, float* o, float* lse, hipStream_t stream);
 
 // Greedy acceptance: per-slice maxima of one node's logits, the tree with
 // depths and ancestor-or-self bits (in the kernel arguments, like the mask

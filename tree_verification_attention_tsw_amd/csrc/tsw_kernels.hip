@@ -27,6 +27,8 @@
 //  * split_valu: float32 or bfloat16 inputs, d = 64 or 128, any row count;
 //    plain FMA dot products in fp32.  Exact fp32 path for float32 inputs and
 //    the fallback for shapes the matrix-core kernel does not cover.
+#include <string.h>
+
 #include <type_traits>
 
 #include "tsw_device.h"
@@ -161,7 +163,8 @@ __global__ __launch_bounds__(256) void split_valu(const SplitArgs a) {
 // ---------------------------------------------------------------------------
 // Log-sum-exp merge of split results
 // ---------------------------------------------------------------------------
-// One wavefront per output row: lanes hold the split LSEs (64 at a time),
+// One wavefront per output row (rows grouped by sequence, each sequence with
+// its own run of splits): lanes hold the split LSEs (64 at a time),
 // wave reductions give the row's LSE, and each lane accumulates d/64
 // consecutive columns over the splits with coalesced loads.  The partial
 // rows do not depend on the LSEs, so the first kMergeChunk of them are
@@ -169,9 +172,9 @@ __global__ __launch_bounds__(256) void split_valu(const SplitArgs a) {
 constexpr int kMergeChunk = 32;
 
 template <int D>
-__global__ __launch_bounds__(256) void lse_merge(int n_splits, int64_t n_rows,
-                                                 const float* __restrict__ part_o,
-                                                 const float* __restrict__ part_lse,
+__global__ __launch_bounds__(256) void lse_merge(const MergeSegs segs, int64_t n_rows,
+                                                 const float* __restrict__ part_o_all,
+                                                 const float* __restrict__ part_lse_all,
                                                  float* __restrict__ o, float* __restrict__ lse) {
     constexpr int PER = D / 64;
     constexpr int CH = kMergeChunk;
@@ -180,19 +183,25 @@ __global__ __launch_bounds__(256) void lse_merge(int n_splits, int64_t n_rows,
     const int lane = threadIdx.x & 63;
     const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     if (r >= n_rows) return;
-    const VT* src = (const VT*)(part_o + r * D) + lane;
-    const int64_t sstride = n_rows * D / PER;      // VT elements between splits
+    // this row's sequence, its splits and its row within a split's block
+    const int seg = (int)(r / segs.rows_per_seg);
+    const int64_t rr = r - (int64_t)seg * segs.rows_per_seg;
+    const int n_splits = segs.base[seg + 1] - segs.base[seg];
+    const float* part_o = part_o_all + (int64_t)segs.base[seg] * segs.rows_per_seg * D;
+    const float* part_lse = part_lse_all + (int64_t)segs.base[seg] * segs.rows_per_seg;
+    const VT* src = (const VT*)(part_o + rr * D) + lane;
+    const int64_t sstride = segs.rows_per_seg * D / PER;      // VT elements between splits
 
     // chunk 0 of the partial rows (splits past the end re-read the last one
     // and get weight 0), issued with the first 64 LSEs
     VT x[CH];
 #pragma unroll
     for (int j = 0; j < CH; ++j) x[j] = src[(int64_t)(j < n_splits ? j : n_splits - 1) * sstride];
-    const float ls0 = lane < n_splits ? part_lse[(int64_t)lane * n_rows + r] : -INFINITY;
+    const float ls0 = lane < n_splits ? part_lse[(int64_t)lane * segs.rows_per_seg + rr] : -INFINITY;
 
     float mx = ls0;
     for (int s0 = 64; s0 < n_splits; s0 += 64)
-        if (s0 + lane < n_splits) mx = fmaxf(mx, part_lse[(int64_t)(s0 + lane) * n_rows + r]);
+        if (s0 + lane < n_splits) mx = fmaxf(mx, part_lse[(int64_t)(s0 + lane) * segs.rows_per_seg + rr]);
 #pragma unroll
     for (int m = 32; m >= 1; m >>= 1) mx = xor_max(mx, m);
     if (mx == -INFINITY) {
@@ -204,7 +213,7 @@ __global__ __launch_bounds__(256) void lse_merge(int n_splits, int64_t n_rows,
     float sum = ls0 == -INFINITY ? 0.0f : exp2f((ls0 - mx) * kL2e);
     for (int s0 = 64; s0 < n_splits; s0 += 64)
         if (s0 + lane < n_splits) {
-            const float ls = part_lse[(int64_t)(s0 + lane) * n_rows + r];
+            const float ls = part_lse[(int64_t)(s0 + lane) * segs.rows_per_seg + rr];
             sum += ls == -INFINITY ? 0.0f : exp2f((ls - mx) * kL2e);
         }
 #pragma unroll
@@ -224,7 +233,7 @@ __global__ __launch_bounds__(256) void lse_merge(int n_splits, int64_t n_rows,
     };
     for (int s0 = 0; s0 < n_splits; s0 += 64) {
         // weight of split s0 + lane (0 past the end)
-        const float ls = s0 == 0 ? ls0 : (s0 + lane < n_splits ? part_lse[(int64_t)(s0 + lane) * n_rows + r] : -INFINITY);
+        const float ls = s0 == 0 ? ls0 : (s0 + lane < n_splits ? part_lse[(int64_t)(s0 + lane) * segs.rows_per_seg + rr] : -INFINITY);
         const float wl = ls == -INFINITY ? 0.0f : exp2f((ls - L) * kL2e);
         const int ng = n_splits - s0 < 64 ? n_splits - s0 : 64;
         for (int c0 = 0; c0 < ng; c0 += CH) {
@@ -298,15 +307,28 @@ hipError_t launch_split_valu(int dtype, int d, bool gather, const SplitArgs& a, 
     return hipErrorInvalidValue;
 }
 
+hipError_t launch_lse_merge_segs(const MergeSegs& segs, int64_t n_rows, const float* part_o,
+                                 const float* part_lse, float* o, float* lse, hipStream_t stream) {
+    if (n_rows == 0) return hipSuccess;
+    const dim3 grid((unsigned)((n_rows + 3) / 4));
+    hipLaunchKernelGGL(lse_merge<128>, grid, dim3(256), 0, stream, segs, n_rows, part_o, part_lse, o, lse);
+    return hipGetLastError();
+}
+
 hipError_t launch_lse_merge(int n_splits, int64_t n_rows, int d, const float* part_o,
                             const float* part_lse, float* o, float* lse, hipStream_t stream) {
     if (n_rows == 0) return hipSuccess;
     if (d == 128 || d == 64) {
+        MergeSegs segs;
+        memset(&segs, 0, sizeof segs);
+        segs.n_seg = 1;
+        segs.rows_per_seg = n_rows;
+        segs.base[1] = n_splits;
         const dim3 grid((unsigned)((n_rows + 3) / 4));
         if (d == 128)
-            hipLaunchKernelGGL(lse_merge<128>, grid, dim3(256), 0, stream, n_splits, n_rows, part_o, part_lse, o, lse);
+            hipLaunchKernelGGL(lse_merge<128>, grid, dim3(256), 0, stream, segs, n_rows, part_o, part_lse, o, lse);
         else
-            hipLaunchKernelGGL(lse_merge<64>, grid, dim3(256), 0, stream, n_splits, n_rows, part_o, part_lse, o, lse);
+            hipLaunchKernelGGL(lse_merge<64>, grid, dim3(256), 0, stream, segs, n_rows, part_o, part_lse, o, lse);
         return hipGetLastError();
     }
     const int64_t n = n_rows * d;

@@ -122,29 +122,48 @@ __device__ __forceinline__ void issue_tile(const SplitArgs& a, const Ctx& cx, in
         }
         return;
     }
+    // sequence position of this lane's row in each of its loads
+    int64_t pos[S::NI];
+#pragma unroll
+    for (int i = 0; i < S::NI; ++i) {
+        const int u = cx.w * S::NI + i;
+        const int grp = u >= S::TK / 4 ? u - S::TK / 4 : u;
+        const int row = grp * 4 + cx.lj;
+        if (pre) {
+            int64_t kk = k0 + row;
+            if (kk >= cx.c1) kk = cx.c0;
+            pos[i] = MODE == kModeGather ? (int64_t)cx.idx_lds[kk - cx.c0] : kk;
+        } else {
+            int jj = (tt - cx.n_pre_tiles) * S::TK + row;
+            if (jj >= a.T) jj = a.T - 1;
+            pos[i] = cx.n_prefix + jj;
+        }
+    }
+    // paged: all page numbers are read from the staged table first, then
+    // every address is one multiply-add on the page number
+    uint32_t page[S::NI];
+    if constexpr (MODE == kModePaged) {
+#pragma unroll
+        for (int i = 0; i < S::NI; ++i) {
+            const int64_t lp = pos[i] >> a.page_shift;
+            const int slot = pre ? (int)(lp - cx.pg0) : cx.npg + (int)(lp - cx.tpg0);
+            page[i] = (uint32_t)cx.idx_lds[slot];
+        }
+    }
 #pragma unroll
     for (int i = 0; i < S::NI; ++i) {
         const int u = cx.w * S::NI + i;
         const bool isv = u >= S::TK / 4;
         const int grp = isv ? u - S::TK / 4 : u;
         const int row = grp * 4 + cx.lj;
-        int64_t pos;
-        if (pre) {
-            int64_t kk = k0 + row;
-            if (kk >= cx.c1) kk = cx.c0;
-            pos = MODE == kModeGather ? (int64_t)cx.idx_lds[kk - cx.c0] : kk;
-        } else {
-            int jj = (tt - cx.n_pre_tiles) * S::TK + row;
-            if (jj >= a.T) jj = a.T - 1;
-            pos = cx.n_prefix + jj;
-        }
-        if constexpr (MODE == kModePaged) {
-            // sequence position -> (page from the staged table, row in page)
-            const int64_t lp = pos >> a.page_shift;
-            const int slot = pre ? (int)(lp - cx.pg0) : cx.npg + (int)(lp - cx.tpg0);
-            pos = ((int64_t)cx.idx_lds[slot] * a.Hkv + cx.g) * a.page_rows + (pos & (a.page_rows - 1));
-        }
-        const char* src = (isv ? cx.vbase : cx.kbase) + pos * S::ROWB + 16 * (cx.li ^ swz(row));
+        const char* base = isv ? cx.vbase : cx.kbase;
+        const uint32_t chunk = 16 * (cx.li ^ swz(row));
+        const char* src;
+        if constexpr (MODE == kModePaged)
+            src = base + (uint64_t)page[i] * (uint64_t)a.page_bytes +
+                  (uint32_t)((pos[i] & (a.page_rows - 1)) * S::ROWB + chunk);
+        else
+            src = base + pos[i] * S::ROWB + chunk;
         char* dst = sbase + (isv ? S::TK * S::ROWB : 0) + grp * 1024;
         __builtin_amdgcn_global_load_lds((const void*)src, (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
     }
@@ -609,27 +628,35 @@ __global__ __launch_bounds__(W * 64, 1) void split_mfma(const SplitArgs a) {
     cx.w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     cx.rg = cx.w / S::KS;
     cx.ks = cx.w % S::KS;
-    cx.split = blockIdx.x;
     cx.g = blockIdx.y;
-    const int b = blockIdx.z;                       // sequence of a paged batch (else 0)
-    int64_t n_keys = a.n_keys, chunk = a.chunk_keys;
+    // paged batch: grid x enumerates every sequence's splits (a run per
+    // sequence, as many as its length needs); otherwise x is the split
+    int b = 0;
+    cx.split = blockIdx.x;
+    int seq_splits = a.n_splits;
+    int64_t n_keys = a.n_keys;
+    int64_t chunk = a.chunk_keys;
     cx.n_prefix = a.n_prefix;
     if constexpr (MODE == kModePaged) {
+        while (b + 1 < a.B && (int)blockIdx.x >= a.seg_base[b + 1]) ++b;
+        cx.split = blockIdx.x - a.seg_base[b];
+        seq_splits = a.seg_base[b + 1] - a.seg_base[b];
         cx.n_prefix = a.npb[b];
         n_keys = cx.n_prefix;
-        chunk = (n_keys + a.n_splits - 1) / a.n_splits;
+        chunk = (n_keys + seq_splits - 1) / seq_splits;
         chunk = (chunk + S::TK - 1) / S::TK * S::TK;
     }
     cx.q = (const __bf16*)a.q + (size_t)b * a.T * a.Hq * 128;
-    cx.row0 = ((int64_t)cx.split * a.B + b) * a.T;
+    cx.row0 = (int64_t)blockIdx.x * a.T;
     cx.c0 = (int64_t)cx.split * chunk;
     if (cx.c0 > n_keys) cx.c0 = n_keys;
     cx.c1 = cx.c0 + chunk < n_keys ? cx.c0 + chunk : n_keys;
     cx.n_pre_tiles = cx.c1 > cx.c0 ? (int)((cx.c1 - cx.c0 + S::TK - 1) / S::TK) : 0;
-    const int n_tail_tiles = cx.split == a.n_splits - 1 ? (a.T + S::TK - 1) / S::TK : 0;
+    const int n_tail_tiles = cx.split == seq_splits - 1 ? (a.T + S::TK - 1) / S::TK : 0;
     cx.n_tiles = cx.n_pre_tiles + n_tail_tiles;
-    // paged caches fold the head into the page row; others offset by head
-    const size_t head_off = MODE == kModePaged ? 0 : (size_t)cx.g * (size_t)a.kv_head_stride * 2;
+    // paged: this head's rows start g * page_rows rows into every page
+    const size_t head_off = MODE == kModePaged ? (size_t)cx.g * a.page_rows * S::ROWB
+                                               : (size_t)cx.g * (size_t)a.kv_head_stride * 2;
     cx.kbase = (const char*)a.k + head_off;
     cx.vbase = (const char*)a.v + head_off;
     int32_t* idx_lds = (int32_t*)(smem + S::RING);
@@ -652,7 +679,7 @@ __global__ __launch_bounds__(W * 64, 1) void split_mfma(const SplitArgs a) {
         cx.pg0 = cx.c0 >> a.page_shift;
         cx.npg = cx.c1 > cx.c0 ? (int)(((cx.c1 - 1) >> a.page_shift) - cx.pg0 + 1) : 0;
         cx.tpg0 = cx.n_prefix >> a.page_shift;
-        const int ntp = cx.split == a.n_splits - 1
+        const int ntp = cx.split == seq_splits - 1
                             ? (int)(((cx.n_prefix + a.T - 1) >> a.page_shift) - cx.tpg0 + 1) : 0;
         for (int i = threadIdx.x; i < cx.npg; i += S::WAVES * 64) idx_lds[i] = table[cx.pg0 + i];
         for (int i = threadIdx.x; i < ntp; i += S::WAVES * 64) idx_lds[cx.npg + i] = table[cx.tpg0 + i];
@@ -673,7 +700,8 @@ __global__ __launch_bounds__(W * 64, 1) void split_mfma(const SplitArgs a) {
 
 template <int W, int R, int NB>
 hipError_t launch(int mode, const SplitArgs& a, int n_kv_heads, hipStream_t stream) {
-    const dim3 grid(a.n_splits, n_kv_heads, a.B);
+    // paged: n_splits counts the splits of all sequences
+    const dim3 grid(a.n_splits, n_kv_heads);
     if (mode == kModeGather)
         hipLaunchKernelGGL((split_mfma<W, R, NB, kModeGather>), grid, dim3(W * 64), 0, stream, a);
     else if (mode == kModePaged)

@@ -159,6 +159,60 @@ ACCEPT_WORKLOADS = {
 }
 
 
+@dataclass
+class PagedWorkload:
+    """A batch of sequences sharing one tree shape, K/V in pages of a pool."""
+    name: str
+    lengths: tuple
+    Hq: int
+    Hkv: int
+    d: int
+    n_nodes: int
+    page_rows: int
+    seed: int
+
+    def parent(self) -> np.ndarray:
+        return kary_tree_parent(self.n_nodes, 3)
+
+    def pages_needed(self):
+        return [-(-(n + self.n_nodes) // self.page_rows) for n in self.lengths]
+
+    def kv_bytes(self) -> int:
+        """K+V bytes one call reads: every sequence's prefix plus its tree rows."""
+        return sum(2 * self.Hkv * (n + self.n_nodes) * self.d * 2 for n in self.lengths)
+
+
+PAGED_WORKLOADS = {
+    # eight GQA-8B sequences of different lengths, 102400 committed tokens in
+    # all (the headline's KV volume), 16-row pages shuffled in the pool
+    "paged_gqa8b_b8": PagedWorkload("paged_gqa8b_b8", lengths=(25600, 19200, 16000, 12800, 9600, 8000,
+                                                               6400, 4800),
+                                    Hq=32, Hkv=8, d=128, n_nodes=full_kary_nodes(3), page_rows=16,
+                                    seed=8000),
+}
+
+
+def make_paged_inputs(w: PagedWorkload, device, seed_offset: int = 0):
+    """q [B, T, Hq, d], K/V page pools [n_pages, Hkv, page_rows, d] (bf16,
+    N(0, 1)), a block table [B, max_pages] over a random permutation of the
+    pages; returns (q, k_pages, v_pages, table)."""
+    g = torch.Generator(device=device)
+    g.manual_seed(w.seed + seed_offset)
+    need = w.pages_needed()
+    n_pages = sum(need)
+    shape = (n_pages, w.Hkv, w.page_rows, w.d)
+    kp = torch.randn(shape, generator=g, device=device).to(torch.bfloat16)
+    vp = torch.randn(shape, generator=g, device=device).to(torch.bfloat16)
+    q = torch.randn((len(w.lengths), w.n_nodes, w.Hq, w.d), generator=g, device=device).to(torch.bfloat16)
+    perm = np.random.default_rng(w.seed + seed_offset).permutation(n_pages).astype(np.int32)
+    table = np.zeros((len(w.lengths), max(need)), dtype=np.int32)
+    at = 0
+    for b, k in enumerate(need):
+        table[b, :k] = perm[at:at + k]
+        at += k
+    return q, kp, vp, torch.from_numpy(table).to(device)
+
+
 def make_accept_inputs(w: AcceptWorkload, device, seed_offset: int = 0):
     """Logits ~ N(0, 1) and draft tokens that repeat the most likely token at
     the parent with probability p_match (else a uniform token)."""
