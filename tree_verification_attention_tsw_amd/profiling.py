@@ -11,8 +11,9 @@ numbers they support:
   elementwise copy of known size run in the same process (bench.py
   ``--copy-calibration-mib``).
 
-The traffic summary records a digest of the kernel sources so that a reader
-(bench.py) can tell whether the counters still describe the current code.
+The summaries record a digest of the split kernel's sources so that a
+reader (bench.py) can tell whether the counters still describe the current
+code.
 
     python -m tree_verification_attention_tsw_amd.profiling stats DIR OUT --command "..."
     python -m tree_verification_attention_tsw_amd.profiling traffic FETCH_DIR WRITE_DIR OUT \\
@@ -30,10 +31,15 @@ ROOT = os.path.dirname(PKG)
 COPY_KERNEL_MARK = "MulFunctor<float>"
 
 
+# The split kernel's sources: its template, instantiation and dispatch
+# units, the device helpers and the argument structures it is launched with.
+SPLIT_KERNEL_SOURCES = ("tsw_mfma_impl.h", "tsw_mfma_inst.hip", "tsw_mfma.hip", "tsw_device.h", "tsw_internal.h")
+
+
 def source_digest():
-    """sha256 over the kernel and C-ABI sources (name + bytes, sorted)."""
+    """sha256 over the split kernel's sources (name + bytes, sorted)."""
     h = hashlib.sha256()
-    files = sorted(glob.glob(os.path.join(PKG, "csrc", "*")) + glob.glob(os.path.join(ROOT, "include", "*.h")))
+    files = sorted(os.path.join(PKG, "csrc", n) for n in SPLIT_KERNEL_SOURCES)
     for f in files:
         h.update(os.path.relpath(f, ROOT).encode())
         with open(f, "rb") as fh:
