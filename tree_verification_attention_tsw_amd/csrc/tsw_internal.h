@@ -48,7 +48,7 @@ struct SplitArgs {
 struct MergeSegs {
     int32_t n_seg;
     int32_t pad_;
-    int64_t rows_per_seg;
+    int64_t rows_per_seg;    // < 2^31 when n_seg > 1 (T * Hq rows)
     int32_t base[65];
 };
 

@@ -171,37 +171,31 @@ __global__ __launch_bounds__(256) void split_valu(const SplitArgs a) {
 // loaded together with the LSEs: a row costs about one memory round trip.
 constexpr int kMergeChunk = 32;
 
+// Output row r from the n_splits partial rows rr of blocks of `stride` rows
+// (part_o / part_lse point at the first split of the row's run).
 template <int D>
-__global__ __launch_bounds__(256) void lse_merge(const MergeSegs segs, int64_t n_rows,
-                                                 const float* __restrict__ part_o_all,
-                                                 const float* __restrict__ part_lse_all,
-                                                 float* __restrict__ o, float* __restrict__ lse) {
+__device__ __forceinline__ void merge_row(int n_splits, int64_t stride, int64_t rr, int64_t r,
+                                          const float* __restrict__ part_o,
+                                          const float* __restrict__ part_lse, float* __restrict__ o,
+                                          float* __restrict__ lse) {
     constexpr int PER = D / 64;
     constexpr int CH = kMergeChunk;
     using VT = typename std::conditional<PER == 2, float2, float>::type;
     constexpr float kL2e = 1.44269504088896340736f;
     const int lane = threadIdx.x & 63;
-    const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (r >= n_rows) return;
-    // this row's sequence, its splits and its row within a split's block
-    const int seg = (int)(r / segs.rows_per_seg);
-    const int64_t rr = r - (int64_t)seg * segs.rows_per_seg;
-    const int n_splits = segs.base[seg + 1] - segs.base[seg];
-    const float* part_o = part_o_all + (int64_t)segs.base[seg] * segs.rows_per_seg * D;
-    const float* part_lse = part_lse_all + (int64_t)segs.base[seg] * segs.rows_per_seg;
     const VT* src = (const VT*)(part_o + rr * D) + lane;
-    const int64_t sstride = segs.rows_per_seg * D / PER;      // VT elements between splits
+    const int64_t sstride = stride * D / PER;      // VT elements between splits
 
     // chunk 0 of the partial rows (splits past the end re-read the last one
     // and get weight 0), issued with the first 64 LSEs
     VT x[CH];
 #pragma unroll
     for (int j = 0; j < CH; ++j) x[j] = src[(int64_t)(j < n_splits ? j : n_splits - 1) * sstride];
-    const float ls0 = lane < n_splits ? part_lse[(int64_t)lane * segs.rows_per_seg + rr] : -INFINITY;
+    const float ls0 = lane < n_splits ? part_lse[(int64_t)lane * stride + rr] : -INFINITY;
 
     float mx = ls0;
     for (int s0 = 64; s0 < n_splits; s0 += 64)
-        if (s0 + lane < n_splits) mx = fmaxf(mx, part_lse[(int64_t)(s0 + lane) * segs.rows_per_seg + rr]);
+        if (s0 + lane < n_splits) mx = fmaxf(mx, part_lse[(int64_t)(s0 + lane) * stride + rr]);
 #pragma unroll
     for (int m = 32; m >= 1; m >>= 1) mx = xor_max(mx, m);
     if (mx == -INFINITY) {
@@ -213,7 +207,7 @@ __global__ __launch_bounds__(256) void lse_merge(const MergeSegs segs, int64_t n
     float sum = ls0 == -INFINITY ? 0.0f : exp2f((ls0 - mx) * kL2e);
     for (int s0 = 64; s0 < n_splits; s0 += 64)
         if (s0 + lane < n_splits) {
-            const float ls = part_lse[(int64_t)(s0 + lane) * segs.rows_per_seg + rr];
+            const float ls = part_lse[(int64_t)(s0 + lane) * stride + rr];
             sum += ls == -INFINITY ? 0.0f : exp2f((ls - mx) * kL2e);
         }
 #pragma unroll
@@ -233,7 +227,7 @@ __global__ __launch_bounds__(256) void lse_merge(const MergeSegs segs, int64_t n
     };
     for (int s0 = 0; s0 < n_splits; s0 += 64) {
         // weight of split s0 + lane (0 past the end)
-        const float ls = s0 == 0 ? ls0 : (s0 + lane < n_splits ? part_lse[(int64_t)(s0 + lane) * segs.rows_per_seg + rr] : -INFINITY);
+        const float ls = s0 == 0 ? ls0 : (s0 + lane < n_splits ? part_lse[(int64_t)(s0 + lane) * stride + rr] : -INFINITY);
         const float wl = ls == -INFINITY ? 0.0f : exp2f((ls - L) * kL2e);
         const int ng = n_splits - s0 < 64 ? n_splits - s0 : 64;
         for (int c0 = 0; c0 < ng; c0 += CH) {
@@ -251,6 +245,31 @@ __global__ __launch_bounds__(256) void lse_merge(const MergeSegs segs, int64_t n
 #pragma unroll
     for (int e = 0; e < PER; ++e) o[r * D + lane * PER + e] = acc[e];
     if (lane == 0) lse[r] = L;
+}
+
+// One sequence: n_splits blocks of n_rows rows.
+template <int D>
+__global__ __launch_bounds__(256) void lse_merge(int n_splits, int64_t n_rows, const float* __restrict__ part_o,
+                                                 const float* __restrict__ part_lse, float* __restrict__ o,
+                                                 float* __restrict__ lse) {
+    const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (r >= n_rows) return;
+    merge_row<D>(n_splits, n_rows, r, r, part_o, part_lse, o, lse);
+}
+
+// Several sequences, each with its own run of splits of rows_per_seg rows.
+template <int D>
+__global__ __launch_bounds__(256) void lse_merge_segs(const MergeSegs segs, int64_t n_rows,
+                                                      const float* __restrict__ part_o,
+                                                      const float* __restrict__ part_lse, float* __restrict__ o,
+                                                      float* __restrict__ lse) {
+    const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (r >= n_rows) return;
+    const int seg = (int)((uint32_t)r / (uint32_t)segs.rows_per_seg);
+    const int64_t rr = r - (int64_t)seg * segs.rows_per_seg;
+    const int64_t first = (int64_t)segs.base[seg] * segs.rows_per_seg;
+    merge_row<D>(segs.base[seg + 1] - segs.base[seg], segs.rows_per_seg, rr, r, part_o + first * D, part_lse + first,
+                 o, lse);
 }
 
 // Any head dim: one thread per output element (used for d other than 64/128).
@@ -311,7 +330,7 @@ hipError_t launch_lse_merge_segs(const MergeSegs& segs, int64_t n_rows, const fl
                                  const float* part_lse, float* o, float* lse, hipStream_t stream) {
     if (n_rows == 0) return hipSuccess;
     const dim3 grid((unsigned)((n_rows + 3) / 4));
-    hipLaunchKernelGGL(lse_merge<128>, grid, dim3(256), 0, stream, segs, n_rows, part_o, part_lse, o, lse);
+    hipLaunchKernelGGL(lse_merge_segs<128>, grid, dim3(256), 0, stream, segs, n_rows, part_o, part_lse, o, lse);
     return hipGetLastError();
 }
 
@@ -319,16 +338,11 @@ hipError_t launch_lse_merge(int n_splits, int64_t n_rows, int d, const float* pa
                             const float* part_lse, float* o, float* lse, hipStream_t stream) {
     if (n_rows == 0) return hipSuccess;
     if (d == 128 || d == 64) {
-        MergeSegs segs;
-        memset(&segs, 0, sizeof segs);
-        segs.n_seg = 1;
-        segs.rows_per_seg = n_rows;
-        segs.base[1] = n_splits;
         const dim3 grid((unsigned)((n_rows + 3) / 4));
         if (d == 128)
-            hipLaunchKernelGGL(lse_merge<128>, grid, dim3(256), 0, stream, segs, n_rows, part_o, part_lse, o, lse);
+            hipLaunchKernelGGL(lse_merge<128>, grid, dim3(256), 0, stream, n_splits, n_rows, part_o, part_lse, o, lse);
         else
-            hipLaunchKernelGGL(lse_merge<64>, grid, dim3(256), 0, stream, segs, n_rows, part_o, part_lse, o, lse);
+            hipLaunchKernelGGL(lse_merge<64>, grid, dim3(256), 0, stream, n_splits, n_rows, part_o, part_lse, o, lse);
         return hipGetLastError();
     }
     const int64_t n = n_rows * d;

@@ -122,50 +122,63 @@ __device__ __forceinline__ void issue_tile(const SplitArgs& a, const Ctx& cx, in
         }
         return;
     }
-    // sequence position of this lane's row in each of its loads
-    int64_t pos[S::NI];
-#pragma unroll
-    for (int i = 0; i < S::NI; ++i) {
-        const int u = cx.w * S::NI + i;
-        const int grp = u >= S::TK / 4 ? u - S::TK / 4 : u;
-        const int row = grp * 4 + cx.lj;
-        if (pre) {
-            int64_t kk = k0 + row;
-            if (kk >= cx.c1) kk = cx.c0;
-            pos[i] = MODE == kModeGather ? (int64_t)cx.idx_lds[kk - cx.c0] : kk;
-        } else {
-            int jj = (tt - cx.n_pre_tiles) * S::TK + row;
-            if (jj >= a.T) jj = a.T - 1;
-            pos[i] = cx.n_prefix + jj;
-        }
-    }
-    // paged: all page numbers are read from the staged table first, then
-    // every address is one multiply-add on the page number
-    uint32_t page[S::NI];
-    if constexpr (MODE == kModePaged) {
+    if constexpr (MODE != kModePaged) {
 #pragma unroll
         for (int i = 0; i < S::NI; ++i) {
+            const int u = cx.w * S::NI + i;
+            const bool isv = u >= S::TK / 4;
+            const int grp = isv ? u - S::TK / 4 : u;
+            const int row = grp * 4 + cx.lj;
+            int64_t pos;
+            if (pre) {
+                int64_t kk = k0 + row;
+                if (kk >= cx.c1) kk = cx.c0;
+                pos = MODE == kModeGather ? (int64_t)cx.idx_lds[kk - cx.c0] : kk;
+            } else {
+                int jj = (tt - cx.n_pre_tiles) * S::TK + row;
+                if (jj >= a.T) jj = a.T - 1;
+                pos = cx.n_prefix + jj;
+            }
+            const char* src = (isv ? cx.vbase : cx.kbase) + pos * S::ROWB + 16 * (cx.li ^ swz(row));
+            char* dst = sbase + (isv ? S::TK * S::ROWB : 0) + grp * 1024;
+            __builtin_amdgcn_global_load_lds((const void*)src, (__attribute__((address_space(3))) void*)dst, 16, 0,
+                                             0);
+        }
+    } else {
+        // paged: every load's page number is read from the staged table
+        // first, then each address is one multiply-add on it
+        int64_t pos[S::NI];
+        uint32_t page[S::NI];
+#pragma unroll
+        for (int i = 0; i < S::NI; ++i) {
+            const int u = cx.w * S::NI + i;
+            const int grp = u >= S::TK / 4 ? u - S::TK / 4 : u;
+            const int row = grp * 4 + cx.lj;
+            if (pre) {
+                int64_t kk = k0 + row;
+                if (kk >= cx.c1) kk = cx.c0;
+                pos[i] = kk;
+            } else {
+                int jj = (tt - cx.n_pre_tiles) * S::TK + row;
+                if (jj >= a.T) jj = a.T - 1;
+                pos[i] = cx.n_prefix + jj;
+            }
             const int64_t lp = pos[i] >> a.page_shift;
             const int slot = pre ? (int)(lp - cx.pg0) : cx.npg + (int)(lp - cx.tpg0);
             page[i] = (uint32_t)cx.idx_lds[slot];
         }
-    }
 #pragma unroll
-    for (int i = 0; i < S::NI; ++i) {
-        const int u = cx.w * S::NI + i;
-        const bool isv = u >= S::TK / 4;
-        const int grp = isv ? u - S::TK / 4 : u;
-        const int row = grp * 4 + cx.lj;
-        const char* base = isv ? cx.vbase : cx.kbase;
-        const uint32_t chunk = 16 * (cx.li ^ swz(row));
-        const char* src;
-        if constexpr (MODE == kModePaged)
-            src = base + (uint64_t)page[i] * (uint64_t)a.page_bytes +
-                  (uint32_t)((pos[i] & (a.page_rows - 1)) * S::ROWB + chunk);
-        else
-            src = base + pos[i] * S::ROWB + chunk;
-        char* dst = sbase + (isv ? S::TK * S::ROWB : 0) + grp * 1024;
-        __builtin_amdgcn_global_load_lds((const void*)src, (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
+        for (int i = 0; i < S::NI; ++i) {
+            const int u = cx.w * S::NI + i;
+            const bool isv = u >= S::TK / 4;
+            const int grp = isv ? u - S::TK / 4 : u;
+            const int row = grp * 4 + cx.lj;
+            const char* src = (isv ? cx.vbase : cx.kbase) + (uint64_t)page[i] * (uint64_t)a.page_bytes +
+                              (uint32_t)((pos[i] & (a.page_rows - 1)) * S::ROWB + 16 * (cx.li ^ swz(row)));
+            char* dst = sbase + (isv ? S::TK * S::ROWB : 0) + grp * 1024;
+            __builtin_amdgcn_global_load_lds((const void*)src, (__attribute__((address_space(3))) void*)dst, 16, 0,
+                                             0);
+        }
     }
 }
 
