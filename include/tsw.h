@@ -193,6 +193,33 @@ int tsw_tree_attn_verify_paged(const tsw_paged_desc* desc, const void* q, const 
                                void* workspace, size_t workspace_bytes, tsw_stream_t stream);
 
 /* ---------------------------------------------------------------------
+ * Partial-cache selection for the next draft pass.  The draft pass keeps the
+ * initial positions and the most important others ("TokenSwift - A framework
+ * for accelerating the generation of ultra-long text" (aiboss88), technical
+ * principles, dynamic KV cache update).  The pages do not define
+ * importance; here it is the attention mass the tree root's query heads put
+ * on each committed position in the verification pass:
+ *   imp[p] = sum_h exp(scale * q[0][h] . k[g(h)][p] - lse[0][h]),  p < n_prefix
+ * (q, k as passed to tsw_tree_attn_verify, lse its output).  The index list
+ * is 0 .. n_keep-1 followed by the n_idx - n_keep positions >= n_keep of
+ * largest importance (equal importance: the lower position first), sorted
+ * ascending: ready for tsw_tree_attn_partial.
+ * ------------------------------------------------------------------- */
+
+/* Workspace bytes (importance scratch) for n_prefix committed positions. */
+int tsw_select_workspace_size(int64_t n_prefix, size_t* bytes);
+
+/* desc as for verification (Hq <= 64, n_prefix < 2^31); k 16-byte aligned.
+ * Writes idx[0 .. min(n_idx, n_prefix)) (device int32).  importance:
+ * optional device float32 [n_prefix] output of imp (NULL: the workspace holds
+ * it, >= tsw_select_workspace_size() bytes).  Errors: TSW_EINVAL,
+ * TSW_EBADINDEX (negative n_keep or n_idx), TSW_EUNSUPPORTED, TSW_ENOSPACE,
+ * TSW_EHIP. */
+int tsw_select_partial(const tsw_attn_desc* desc, const void* q, const void* k, const float* lse,
+                       int64_t n_keep, int64_t n_idx, int32_t* idx, float* importance, void* workspace,
+                       size_t workspace_bytes, tsw_stream_t stream);
+
+/* ---------------------------------------------------------------------
  * After verification: greedy acceptance and accepted-path KV compaction.
  *
  * The target model's logits at each tree node give its most likely next

@@ -236,3 +236,21 @@ def test_paged_argument_errors(L):
     assert _paged(L, _pdesc(), q=ctypes.c_void_p(0x10008)) == EINVAL
     n = ctypes.c_size_t(0)
     assert L.tsw_paged_workspace_size(ctypes.byref(_pdesc(B=0)), None, ctypes.byref(n)) == EINVAL
+
+
+def test_select_argument_errors(L):
+    def call(desc=None, q=FAKE, k=FAKE, lse=FAKE, n_keep=128, n_idx=4096, idx=FAKE, imp=None, ws=FAKE):
+        d = desc if desc is not None else _desc()
+        return L.tsw_select_partial(ctypes.byref(d), q, k, lse, n_keep, n_idx, idx, imp, ws, 1 << 30, None)
+    assert call(n_keep=-1) == EBADINDEX
+    assert call(n_idx=-1) == EBADINDEX
+    assert call(q=None) == EINVAL
+    assert call(lse=None) == EINVAL
+    assert call(idx=None) == EINVAL
+    assert call(ws=None) == EINVAL                        # no importance output and no workspace
+    assert call(k=ctypes.c_void_p(0x10008)) == EINVAL     # not 16-byte aligned
+    assert call(desc=_desc(Hq=128, Hkv=8)) == EUNSUP     # more query heads than the kernel holds
+    assert call(desc=_desc(d=96)) == EUNSUP
+    n = ctypes.c_size_t(0)
+    assert L.tsw_select_workspace_size(-1, ctypes.byref(n)) == EINVAL
+    assert L.tsw_select_workspace_size(1000, ctypes.byref(n)) == TSW_OK and n.value >= 4000

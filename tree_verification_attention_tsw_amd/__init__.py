@@ -3,8 +3,9 @@
 TokenSwift verifies a 3-ary tree of drafted tokens in one forward pass with
 tree-structured attention over the full KV cache, and drafts with the same
 model over a partial cache.  This package is the attention step of both
-passes, plus the greedy acceptance of the verified tree and the compaction
-of the accepted path's K/V rows: a C-ABI library of hand-written HIP kernels
+passes, plus the greedy acceptance of the verified tree, the compaction of
+the accepted path's K/V rows and the selection of the next draft pass's
+partial cache: a C-ABI library of hand-written HIP kernels
 (include/tsw.h, libtsw.so) and this thin Python binding.  PyTorch supplies
 device memory and streams only.
 """
@@ -14,4 +15,5 @@ from ._binding import (  # noqa: F401
     tree_mask, workspace_size, PreparedCall, prepare_merge, prepare_split, prepare_verify,
     accept_workspace_size, accept_greedy, prepare_accept, kv_compact, prepare_compact,
     PagedDesc, make_paged_desc, paged_workspace_size, tree_attn_verify_paged, prepare_verify_paged,
+    select_workspace_size, select_partial, prepare_select,
 )

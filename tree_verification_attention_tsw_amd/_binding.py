@@ -68,6 +68,8 @@ def lib():
     PD = ctypes.POINTER(PagedDesc)
     L.tsw_paged_workspace_size.argtypes = [PD, vp, ctypes.POINTER(sz)]
     L.tsw_tree_attn_verify_paged.argtypes = [PD, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.tsw_select_workspace_size.argtypes = [i64, ctypes.POINTER(sz)]
+    L.tsw_select_partial.argtypes = [D, vp, vp, vp, i64, i64, vp, vp, vp, sz, vp]
     L.tsw_accept_workspace_size.argtypes = [i32, i64, ctypes.POINTER(sz)]
     L.tsw_accept_greedy.argtypes = [vp, i32, vp, i64, i32, vp, vp, vp, sz, vp]
     L.tsw_kv_compact.argtypes = [vp, vp, i32, i64, i32, i32, i32, i64, i64, i32, vp, vp]
@@ -76,7 +78,8 @@ def lib():
     for name in ("tsw_tree_mask_build", "tsw_plan_splits", "tsw_workspace_size",
                  "tsw_tree_attn_verify", "tsw_tree_attn_partial", "tsw_tree_attn_split",
                  "tsw_lse_merge", "tsw_accept_workspace_size", "tsw_accept_greedy",
-                 "tsw_kv_compact", "tsw_paged_workspace_size", "tsw_tree_attn_verify_paged"):
+                 "tsw_kv_compact", "tsw_paged_workspace_size", "tsw_tree_attn_verify_paged",
+                 "tsw_select_workspace_size", "tsw_select_partial"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L
@@ -466,3 +469,41 @@ def prepare_verify_paged(q, k_pages, v_pages, block_table, n_prefix, parent, o, 
     args, keep = _paged_args(q, k_pages, v_pages, block_table, n_prefix, parent, o, lse, workspace, scale,
                              stream)
     return PreparedCall(lib().tsw_tree_attn_verify_paged, args, "tsw_tree_attn_verify_paged", keep)
+
+
+# ------------------------------------------------------------ partial-cache selection
+
+def select_workspace_size(n_prefix):
+    n = ctypes.c_size_t(0)
+    _check(lib().tsw_select_workspace_size(int(n_prefix), ctypes.byref(n)), "tsw_select_workspace_size")
+    return n.value
+
+
+def _select_args(q, k, lse, n_prefix, n_keep, n_idx, idx, importance, workspace, scale, stream):
+    _check_tensors(q, k, k)
+    if lse.dtype != torch.float32 or not lse.is_cuda or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 GPU tensor")
+    desc = make_desc(q, k, n_prefix, scale)
+    n_out = min(int(n_idx), int(n_prefix))
+    if idx is None:
+        idx = torch.empty(max(n_out, 1), dtype=torch.int32, device=q.device)
+    if importance is None and workspace is None:
+        workspace = torch.empty(select_workspace_size(n_prefix), dtype=torch.uint8, device=q.device)
+    st = ctypes.c_void_p(stream.cuda_stream if stream is not None
+                         else torch.cuda.current_stream(q.device).cuda_stream)
+    args = (ctypes.byref(desc), _dev_ptr(q), _dev_ptr(k), _dev_ptr(lse), int(n_keep), int(n_idx), _dev_ptr(idx),
+            _dev_ptr(importance), _dev_ptr(workspace), workspace.numel() if workspace is not None else 0, st)
+    return args, (desc, idx, importance, workspace), n_out
+
+
+def select_partial(q, k, lse, n_prefix, n_keep, n_idx, scale=None, importance=None, idx=None, workspace=None):
+    """Index list for the next draft pass: (idx int32 [min(n_idx, n_prefix)], importance or None)."""
+    args, keep, n_out = _select_args(q, k, lse, n_prefix, n_keep, n_idx, idx, importance, workspace, scale, None)
+    _check(lib().tsw_select_partial(*args), "tsw_select_partial")
+    return keep[1][:n_out], importance
+
+
+def prepare_select(q, k, lse, n_prefix, n_keep, n_idx, idx, importance=None, workspace=None, scale=None,
+                   stream=None):
+    args, keep, _ = _select_args(q, k, lse, n_prefix, n_keep, n_idx, idx, importance, workspace, scale, stream)
+    return PreparedCall(lib().tsw_select_partial, args, "tsw_select_partial", keep)

@@ -504,6 +504,52 @@ int tsw_tree_attn_verify_paged(const tsw_paged_desc* desc, const void* q, const 
                                                  (hipStream_t)stream));
 }
 
+int tsw_select_workspace_size(int64_t n_prefix, size_t* bytes) {
+    if (!bytes || n_prefix < 0 || n_prefix > INT32_MAX) return TSW_EINVAL;
+    *bytes = align256((size_t)n_prefix * sizeof(float));
+    if (*bytes < 256) *bytes = 256;
+    return TSW_OK;
+}
+
+int tsw_select_partial(const tsw_attn_desc* desc, const void* q, const void* k, const float* lse, int64_t n_keep,
+                       int64_t n_idx, int32_t* idx, float* importance, void* workspace, size_t workspace_bytes,
+                       tsw_stream_t stream) {
+    int rc = check_desc(desc);
+    if (rc != TSW_OK) return rc;
+    if (desc->Hq > tsw::kSelectMaxHeads) return TSW_EUNSUPPORTED;
+    if (desc->n_prefix > INT32_MAX) return TSW_EUNSUPPORTED;
+    if (n_keep < 0 || n_idx < 0) return TSW_EBADINDEX;
+    if (!q || !k || !lse) return TSW_EINVAL;
+    const int64_t n_out = n_idx < desc->n_prefix ? n_idx : desc->n_prefix;
+    if (n_out > 0 && !idx) return TSW_EINVAL;
+    const int esz = desc->dtype == TSW_DTYPE_F32 ? 4 : 2;
+    if ((uintptr_t)k & 15) return TSW_EINVAL;
+    if ((desc->kv_head_stride * esz) % 16) return TSW_EINVAL;
+    float* imp = importance;
+    if (!imp) {
+        if (!workspace) return TSW_EINVAL;
+        if (workspace_bytes < (size_t)desc->n_prefix * sizeof(float)) return TSW_ENOSPACE;
+        imp = (float*)workspace;
+    }
+    tsw::SelectArgs a;
+    memset(&a, 0, sizeof a);
+    a.q = q;
+    a.k = k;
+    a.lse = lse;
+    a.n_prefix = desc->n_prefix;
+    a.kv_head_stride = desc->kv_head_stride;
+    a.Hq = desc->Hq;
+    a.Hkv = desc->Hkv;
+    a.G = desc->Hq / desc->Hkv;
+    a.d = desc->d;
+    a.dtype = desc->dtype == TSW_DTYPE_F32 ? 0 : 1;
+    a.scale = desc->scale;
+    rc = hip_status(tsw::launch_importance(a, imp, (hipStream_t)stream));
+    if (rc != TSW_OK || n_out == 0) return rc;
+    const int64_t keep = n_keep < n_out ? n_keep : n_out;
+    return hip_status(tsw::launch_select(imp, desc->n_prefix, keep, n_out, idx, (hipStream_t)stream));
+}
+
 const char* tsw_status_str(int status) {
     switch (status) {
         case TSW_OK: return "ok";

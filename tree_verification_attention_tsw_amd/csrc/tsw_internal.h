@@ -104,6 +104,22 @@ hipError_t launch_accept(const AcceptArgs& a, const void* logits, int logits_dty
 hipError_t launch_kv_compact(const CompactArgs& a, int n_layers, int n_kv_heads, const int32_t* result,
                              hipStream_t stream);
 
+// Importance of committed positions (node 0's attention mass) and the
+// draft pass's index selection.
+constexpr int kSelectChunk = 256;      // keys per importance work-group
+constexpr int kSelectMaxHeads = 64;    // query heads held in LDS
+struct SelectArgs {
+    const void* q;           // [T][Hq][d]; node 0's row is used
+    const void* k;           // [Hkv][rows][d]
+    const float* lse;        // [T][Hq]; node 0's row is used
+    int64_t n_prefix, kv_head_stride;
+    int32_t Hq, Hkv, G, d, dtype;
+    float scale;
+};
+hipError_t launch_importance(const SelectArgs& a, float* imp, hipStream_t stream);
+hipError_t launch_select(const float* imp, int64_t n_prefix, int64_t n_keep, int64_t n_out, int32_t* idx,
+                         hipStream_t stream);
+
 // Key tile of the vector-ALU kernel and its query rows per work-group.
 constexpr int kValuTile = 64;
 constexpr int kValuRows = 16;
