@@ -206,13 +206,15 @@ int tsw_tree_attn_verify_paged(const tsw_paged_desc* desc, const void* q, const 
  * ascending: ready for tsw_tree_attn_partial.
  * ------------------------------------------------------------------- */
 
-/* Workspace bytes (importance scratch) for n_prefix committed positions. */
+/* Workspace bytes for n_prefix committed positions (importance values and
+ * selection counts). */
 int tsw_select_workspace_size(int64_t n_prefix, size_t* bytes);
 
 /* desc as for verification (Hq <= 64, n_prefix < 2^31); k 16-byte aligned.
  * Writes idx[0 .. min(n_idx, n_prefix)) (device int32).  importance:
- * optional device float32 [n_prefix] output of imp (NULL: the workspace holds
- * it, >= tsw_select_workspace_size() bytes).  Errors: TSW_EINVAL,
+ * optional device float32 [n_prefix] output of imp (NULL: kept in the
+ * workspace).  workspace: device, 256-byte aligned, >=
+ * tsw_select_workspace_size() bytes, scratch.  Errors: TSW_EINVAL,
  * TSW_EBADINDEX (negative n_keep or n_idx), TSW_EUNSUPPORTED, TSW_ENOSPACE,
  * TSW_EHIP. */
 int tsw_select_partial(const tsw_attn_desc* desc, const void* q, const void* k, const float* lse,

@@ -247,7 +247,7 @@ def test_select_argument_errors(L):
     assert call(q=None) == EINVAL
     assert call(lse=None) == EINVAL
     assert call(idx=None) == EINVAL
-    assert call(ws=None) == EINVAL                        # no importance output and no workspace
+    assert call(ws=None) == EINVAL                        # no workspace
     assert call(k=ctypes.c_void_p(0x10008)) == EINVAL     # not 16-byte aligned
     assert call(desc=_desc(Hq=128, Hkv=8)) == EUNSUP     # more query heads than the kernel holds
     assert call(desc=_desc(d=96)) == EUNSUP

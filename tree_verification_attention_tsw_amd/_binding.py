@@ -487,7 +487,7 @@ def _select_args(q, k, lse, n_prefix, n_keep, n_idx, idx, importance, workspace,
     n_out = min(int(n_idx), int(n_prefix))
     if idx is None:
         idx = torch.empty(max(n_out, 1), dtype=torch.int32, device=q.device)
-    if importance is None and workspace is None:
+    if workspace is None:
         workspace = torch.empty(select_workspace_size(n_prefix), dtype=torch.uint8, device=q.device)
     st = ctypes.c_void_p(stream.cuda_stream if stream is not None
                          else torch.cuda.current_stream(q.device).cuda_stream)

@@ -506,7 +506,7 @@ int tsw_tree_attn_verify_paged(const tsw_paged_desc* desc, const void* q, const 
 
 int tsw_select_workspace_size(int64_t n_prefix, size_t* bytes) {
     if (!bytes || n_prefix < 0 || n_prefix > INT32_MAX) return TSW_EINVAL;
-    *bytes = align256((size_t)n_prefix * sizeof(float));
+    *bytes = align256((size_t)n_prefix * sizeof(float)) + align256(tsw::select_scratch_bytes(n_prefix));
     if (*bytes < 256) *bytes = 256;
     return TSW_OK;
 }
@@ -525,12 +525,12 @@ int tsw_select_partial(const tsw_attn_desc* desc, const void* q, const void* k, 
     const int esz = desc->dtype == TSW_DTYPE_F32 ? 4 : 2;
     if ((uintptr_t)k & 15) return TSW_EINVAL;
     if ((desc->kv_head_stride * esz) % 16) return TSW_EINVAL;
-    float* imp = importance;
-    if (!imp) {
-        if (!workspace) return TSW_EINVAL;
-        if (workspace_bytes < (size_t)desc->n_prefix * sizeof(float)) return TSW_ENOSPACE;
-        imp = (float*)workspace;
-    }
+    if (!workspace) return TSW_EINVAL;
+    if ((uintptr_t)workspace & 255) return TSW_EINVAL;
+    const size_t imp_bytes = align256((size_t)desc->n_prefix * sizeof(float));
+    if (workspace_bytes < imp_bytes + tsw::select_scratch_bytes(desc->n_prefix)) return TSW_ENOSPACE;
+    float* imp = importance ? importance : (float*)workspace;
+    uint32_t* scratch = (uint32_t*)((char*)workspace + imp_bytes);
     tsw::SelectArgs a;
     memset(&a, 0, sizeof a);
     a.q = q;
@@ -547,7 +547,7 @@ int tsw_select_partial(const tsw_attn_desc* desc, const void* q, const void* k, 
     rc = hip_status(tsw::launch_importance(a, imp, (hipStream_t)stream));
     if (rc != TSW_OK || n_out == 0) return rc;
     const int64_t keep = n_keep < n_out ? n_keep : n_out;
-    return hip_status(tsw::launch_select(imp, desc->n_prefix, keep, n_out, idx, (hipStream_t)stream));
+    return hip_status(tsw::launch_select(imp, desc->n_prefix, keep, n_out, idx, scratch, (hipStream_t)stream));
 }
 
 const char* tsw_status_str(int status) {

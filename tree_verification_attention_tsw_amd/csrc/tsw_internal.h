@@ -117,8 +117,10 @@ struct SelectArgs {
     float scale;
 };
 hipError_t launch_importance(const SelectArgs& a, float* imp, hipStream_t stream);
+constexpr int64_t kSelBlock = 4096;    // candidates per selection work-group
+size_t select_scratch_bytes(int64_t n_prefix);
 hipError_t launch_select(const float* imp, int64_t n_prefix, int64_t n_keep, int64_t n_out, int32_t* idx,
-                         hipStream_t stream);
+                         uint32_t* scratch, hipStream_t stream);
 
 // Key tile of the vector-ALU kernel and its query rows per work-group.
 constexpr int kValuTile = 64;

@@ -54,8 +54,24 @@ def _find(d, suffix):
     return hits[-1]
 
 
+def _is_ours(name):
+    return "tsw::" in name or name.startswith("_ZN3tsw")
+
+
 def _short(name):
     """'void tsw::mfma::split_mfma<8, 4, 3, false>(tsw::SplitArgs)' -> 'split_mfma<8, 4, 3, false>'."""
+    if name.startswith("_ZN3tsw"):
+        # mangled (a template in an anonymous namespace): the last of the
+        # length-prefixed names of the nested-name, template arguments dropped
+        i, last = 3, name
+        while i < len(name) and name[i].isdigit():
+            j = i
+            while name[j].isdigit():
+                j += 1
+            n = int(name[i:j])
+            last = name[j:j + n]
+            i = j + n
+        return last + "<...>"
     n = name.replace("(anonymous namespace)::", "").split("(")[0]
     if n.startswith("void "):
         n = n[5:]
@@ -66,7 +82,7 @@ def kernel_stats(d):
     rows = list(csv.DictReader(open(_find(d, "_kernel_stats.csv"))))
     out = []
     for r in rows:
-        if "tsw::" not in r["Name"]:
+        if not _is_ours(r["Name"]):
             continue
         out.append((_short(r["Name"]), int(r["Calls"]), float(r["AverageNs"]) / 1e3,
                     float(r["MinNs"]) / 1e3, float(r["MaxNs"]) / 1e3))

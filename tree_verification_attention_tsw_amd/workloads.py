@@ -213,6 +213,20 @@ def make_paged_inputs(w: PagedWorkload, device, seed_offset: int = 0):
     return q, kp, vp, torch.from_numpy(table).to(device)
 
 
+@dataclass
+class SelectWorkload:
+    """Importance of every committed position and the draft pass's index list."""
+    name: str
+    attn: str          # the verification workload whose q, k, lse feed it
+    n_keep: int
+    n_idx: int
+
+
+SELECT_WORKLOADS = {
+    "select_gqa8b_100k": SelectWorkload("select_gqa8b_100k", attn="gqa8b_100k", n_keep=128, n_idx=4096),
+}
+
+
 def make_accept_inputs(w: AcceptWorkload, device, seed_offset: int = 0):
     """Logits ~ N(0, 1) and draft tokens that repeat the most likely token at
     the parent with probability p_match (else a uniform token)."""
