@@ -221,6 +221,21 @@ int tsw_select_partial(const tsw_attn_desc* desc, const void* q, const void* k, 
                        int64_t n_keep, int64_t n_idx, int32_t* idx, float* importance, void* workspace,
                        size_t workspace_bytes, tsw_stream_t stream);
 
+/* Verification and selection in one call: tsw_tree_attn_verify's o and lse,
+ * then tsw_select_partial's idx and importance for the same desc, q and k.
+ * On the matrix-core path the verification kernel writes the root row's
+ * scores dot(q[0][h], k[g(h)][p]) (p < n_prefix) to the workspace as it
+ * streams K, and the importance is formed from them, so K is read once;
+ * otherwise the importance is computed from q and k as in
+ * tsw_select_partial.  Selection arguments and errors as for
+ * tsw_select_partial, the rest as for tsw_tree_attn_verify; workspace:
+ * device, 256-byte aligned, >= tsw_verify_select_workspace_size() bytes. */
+int tsw_verify_select_workspace_size(const tsw_attn_desc* desc, size_t* bytes);
+int tsw_tree_attn_verify_select(const tsw_attn_desc* desc, const void* q, const void* k, const void* v,
+                                const int32_t* parent, float* o, float* lse, int64_t n_keep, int64_t n_idx,
+                                int32_t* idx, float* importance, void* workspace, size_t workspace_bytes,
+                                tsw_stream_t stream);
+
 /* ---------------------------------------------------------------------
  * After verification: greedy acceptance and accepted-path KV compaction.
  *

@@ -254,3 +254,28 @@ def test_select_argument_errors(L):
     n = ctypes.c_size_t(0)
     assert L.tsw_select_workspace_size(-1, ctypes.byref(n)) == EINVAL
     assert L.tsw_select_workspace_size(1000, ctypes.byref(n)) == TSW_OK and n.value >= 4000
+
+
+def test_verify_select_argument_errors(L):
+    def call(desc=None, q=FAKE, k=FAKE, v=FAKE, parent=PARENT, o=FAKE, lse=FAKE, n_keep=128, n_idx=4096,
+             idx=FAKE, ws=FAKE):
+        d = desc if desc is not None else _desc()
+        p = parent.ctypes.data_as(ctypes.c_void_p) if parent is not None else None
+        return L.tsw_tree_attn_verify_select(ctypes.byref(d), q, k, v, p, o, lse, n_keep, n_idx, idx, None, ws,
+                                             1 << 30, None)
+    assert call(n_keep=-1) == EBADINDEX
+    assert call(n_idx=-1) == EBADINDEX
+    assert call(q=None) == EINVAL
+    assert call(v=None) == EINVAL
+    assert call(parent=None) == EINVAL
+    assert call(o=None) == EINVAL
+    assert call(idx=None) == EINVAL
+    assert call(ws=None) == EINVAL
+    assert call(ws=ctypes.c_void_p(0x10080)) == EINVAL    # workspace not 256-byte aligned
+    assert call(k=ctypes.c_void_p(0x10008)) == EINVAL
+    bad = PARENT.copy()
+    bad[5] = 7                                            # a parent after its child
+    assert call(parent=bad) == EBADTREE
+    assert call(desc=_desc(Hq=128, Hkv=8)) == EUNSUP
+    assert call(desc=_desc(d=96)) == EUNSUP
+    assert L.tsw_verify_select_workspace_size(ctypes.byref(_desc()), None) == EINVAL

@@ -97,3 +97,68 @@ def test_selected_list_feeds_partial_attention():
                                     1 / np.sqrt(d), idx=idx.cpu().numpy(), nthreads=NTHREADS)
     assert float(np.max(np.abs(o.cpu().double().numpy() - o_ref))) <= 4e-3
     assert float(np.max(np.abs(lse.cpu().double().numpy() - l_ref))) <= 4e-3
+
+
+def check_selection(imp_gpu, imp_ref, idx, n_prefix, n_keep, n_idx):
+    if n_prefix:
+        rel = float(np.max(np.abs(imp_gpu - imp_ref) / np.maximum(imp_ref, 1e-30)))
+        say("  importance max rel err %.3g" % rel)
+        assert rel <= 1e-4
+    got = idx.cpu().numpy().tolist()
+    assert got == sel.select(imp_gpu, n_prefix, n_keep, n_idx).tolist()
+
+
+@pytest.mark.parametrize("T,Hq,Hkv,d,n_prefix,n_keep,n_idx,dtype", [
+    (40, 32, 8, 128, 102400, 128, 4096, "bf16"),  # root scores from the split kernel
+    (40, 40, 8, 128, 20003, 128, 4096, "bf16"),   # ragged prefix end, G = 5
+    (13, 32, 32, 128, 9000, 64, 1000, "bf16"),    # G = 1
+    (4, 32, 1, 128, 5000, 16, 300, "bf16"),       # G = 32: importance from K
+    (13, 4, 4, 64, 3000, 16, 500, "f32"),         # vector-ALU verification
+    (4, 8, 2, 128, 300, 128, 4096, "bf16"),       # the whole prefix
+    (4, 8, 2, 128, 300, 200, 100, "bf16"),        # more kept than asked
+    (4, 8, 2, 128, 300, 10, 0, "bf16"),           # nothing asked
+])
+def test_verify_select_matches_verify_and_oracle(T, Hq, Hkv, d, n_prefix, n_keep, n_idx, dtype):
+    """The combined call gives verification's o and lse bit for bit, and the
+    selection to the same bar as the separate call."""
+    tdt = torch.float32 if dtype == "f32" else torch.bfloat16
+    seed = 7 + n_prefix
+    q = gen((T, Hq, d), seed, tdt)
+    k = gen((Hkv, n_prefix + T, d), seed + 1, tdt)
+    v = gen((Hkv, n_prefix + T, d), seed + 2, tdt)
+    parent = wl.kary_tree_parent(T, 3)
+    imp = torch.full((max(n_prefix, 1),), float("nan"), dtype=torch.float32, device="cuda")
+    o, lse, idx, _ = tsw.tree_attn_verify_select(q, k, v, parent, n_prefix, n_keep, n_idx, importance=imp)
+    o_ref, lse_ref = tsw.tree_attn_verify(q, k, v, parent, n_prefix)
+    torch.cuda.synchronize()
+    say("verify_select T=%d Hq=%d Hkv=%d d=%d n_prefix=%d keep=%d n_idx=%d %s" % (T, Hq, Hkv, d, n_prefix,
+                                                                                n_keep, n_idx, dtype))
+    assert torch.equal(o, o_ref) and torch.equal(lse, lse_ref)
+    imp_gpu = imp[:n_prefix].cpu().numpy().astype(np.float64)
+    imp_ref = sel.importance(wl.oracle_view(q), wl.oracle_view(k), lse.cpu().numpy(), n_prefix, 1 / np.sqrt(d))
+    check_selection(imp_gpu, imp_ref, idx, n_prefix, n_keep, n_idx)
+
+
+def test_verify_select_repeated_calls_share_workspace():
+    """Two calls in a row on one workspace (the digit totals are cleared by
+    each call), the second smaller."""
+    T, Hq, Hkv, d = 40, 32, 8, 128
+    ws = torch.empty(tsw.verify_select_workspace_size(gen((T, Hq, d), 1, torch.bfloat16),
+                                                      gen((Hkv, 60040, d), 2, torch.bfloat16), 60000),
+                     dtype=torch.uint8, device="cuda")
+    for n_prefix, seed in ((60000, 21), (33333, 22)):
+        q = gen((T, Hq, d), seed, torch.bfloat16)
+        k = gen((Hkv, n_prefix + T, d), seed + 1, torch.bfloat16)
+        v = gen((Hkv, n_prefix + T, d), seed + 2, torch.bfloat16)
+        parent = wl.kary_tree_parent(T, 3)
+        imp = torch.empty(n_prefix, dtype=torch.float32, device="cuda")
+        need = tsw.verify_select_workspace_size(q, k, n_prefix)
+        assert need <= ws.numel()
+        _, lse, idx, _ = tsw.tree_attn_verify_select(q, k, v, parent, n_prefix, 128, 4096, importance=imp,
+                                                     workspace=ws)
+        torch.cuda.synchronize()
+        say("verify_select repeat n_prefix=%d" % n_prefix)
+        imp_gpu = imp.cpu().numpy().astype(np.float64)
+        imp_ref = sel.importance(wl.oracle_view(q), wl.oracle_view(k), lse.cpu().numpy(), n_prefix,
+                                 1 / np.sqrt(d))
+        check_selection(imp_gpu, imp_ref, idx, n_prefix, 128, 4096)

@@ -16,4 +16,5 @@ from ._binding import (  # noqa: F401
     accept_workspace_size, accept_greedy, prepare_accept, kv_compact, prepare_compact,
     PagedDesc, make_paged_desc, paged_workspace_size, tree_attn_verify_paged, prepare_verify_paged,
     select_workspace_size, select_partial, prepare_select,
+    verify_select_workspace_size, tree_attn_verify_select, prepare_verify_select,
 )

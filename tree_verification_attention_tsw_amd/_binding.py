@@ -70,6 +70,8 @@ def lib():
     L.tsw_tree_attn_verify_paged.argtypes = [PD, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.tsw_select_workspace_size.argtypes = [i64, ctypes.POINTER(sz)]
     L.tsw_select_partial.argtypes = [D, vp, vp, vp, i64, i64, vp, vp, vp, sz, vp]
+    L.tsw_verify_select_workspace_size.argtypes = [D, ctypes.POINTER(sz)]
+    L.tsw_tree_attn_verify_select.argtypes = [D, vp, vp, vp, vp, vp, vp, i64, i64, vp, vp, vp, sz, vp]
     L.tsw_accept_workspace_size.argtypes = [i32, i64, ctypes.POINTER(sz)]
     L.tsw_accept_greedy.argtypes = [vp, i32, vp, i64, i32, vp, vp, vp, sz, vp]
     L.tsw_kv_compact.argtypes = [vp, vp, i32, i64, i32, i32, i32, i64, i64, i32, vp, vp]
@@ -507,3 +509,53 @@ def prepare_select(q, k, lse, n_prefix, n_keep, n_idx, idx, importance=None, wor
                    stream=None):
     args, keep, _ = _select_args(q, k, lse, n_prefix, n_keep, n_idx, idx, importance, workspace, scale, stream)
     return PreparedCall(lib().tsw_select_partial, args, "tsw_select_partial", keep)
+
+
+def verify_select_workspace_size(q, k, n_prefix, scale=None, impl="auto"):
+    desc = make_desc(q, k, n_prefix, scale, impl)
+    n = ctypes.c_size_t(0)
+    _check(lib().tsw_verify_select_workspace_size(ctypes.byref(desc), ctypes.byref(n)),
+           "tsw_verify_select_workspace_size")
+    return n.value
+
+
+def _verify_select_args(q, k, v, parent, n_prefix, n_keep, n_idx, o, lse, idx, importance, workspace, scale,
+                        impl, stream):
+    _check_tensors(q, k, v)
+    T, Hq, d = q.shape
+    desc = make_desc(q, k, n_prefix, scale, impl)
+    if o is None:
+        o = torch.empty((T, Hq, d), dtype=torch.float32, device=q.device)
+    if lse is None:
+        lse = torch.empty((T, Hq), dtype=torch.float32, device=q.device)
+    n_out = min(int(n_idx), int(n_prefix))
+    if idx is None:
+        idx = torch.empty(max(n_out, 1), dtype=torch.int32, device=q.device)
+    if workspace is None:
+        workspace = torch.empty(verify_select_workspace_size(q, k, n_prefix, scale, impl), dtype=torch.uint8,
+                                device=q.device)
+    p = _parent_arr(parent)
+    st = ctypes.c_void_p(stream.cuda_stream if stream is not None
+                         else torch.cuda.current_stream(q.device).cuda_stream)
+    args = (ctypes.byref(desc), _dev_ptr(q), _dev_ptr(k), _dev_ptr(v), _np_ptr(p), _dev_ptr(o), _dev_ptr(lse),
+            int(n_keep), int(n_idx), _dev_ptr(idx), _dev_ptr(importance), _dev_ptr(workspace), workspace.numel(),
+            st)
+    return args, (desc, p, o, lse, idx, importance, workspace), n_out
+
+
+def tree_attn_verify_select(q, k, v, parent, n_prefix, n_keep, n_idx, scale=None, impl="auto", out=None,
+                            idx=None, importance=None, workspace=None):
+    """Verification plus the next draft pass's index list from the same pass:
+    (o, lse, idx [min(n_idx, n_prefix)], importance or None)."""
+    o, lse = out if out is not None else (None, None)
+    args, keep, n_out = _verify_select_args(q, k, v, parent, n_prefix, n_keep, n_idx, o, lse, idx, importance,
+                                            workspace, scale, impl, None)
+    _check(lib().tsw_tree_attn_verify_select(*args), "tsw_tree_attn_verify_select")
+    return keep[2], keep[3], keep[4][:n_out], importance
+
+
+def prepare_verify_select(q, k, v, parent, n_prefix, n_keep, n_idx, o, lse, idx, importance=None,
+                          workspace=None, scale=None, impl="auto", stream=None):
+    args, keep, _ = _verify_select_args(q, k, v, parent, n_prefix, n_keep, n_idx, o, lse, idx, importance,
+                                        workspace, scale, impl, stream)
+    return PreparedCall(lib().tsw_tree_attn_verify_select, args, "tsw_tree_attn_verify_select", keep)

@@ -138,9 +138,12 @@ size_t ws_bytes_for(const tsw_attn_desc* d, int32_t n_splits) {
 
 int hip_status(hipError_t e) { return e == hipSuccess ? TSW_OK : TSW_EHIP; }
 
+// root_s (verify only): also write the root row's scores there, one row of
+// root_stride floats per query head (matrix-core kernel only).
 int run_split(const tsw_attn_desc* d, const void* q, const void* k, const void* v,
               const int32_t* parent, const int32_t* idx, int64_t n_idx, int32_t n_splits,
-              float* part_o, float* part_lse, hipStream_t stream) {
+              float* part_o, float* part_lse, hipStream_t stream, float* root_s = nullptr,
+              int64_t root_stride = 0, uint32_t* root_clear = nullptr) {
     const bool gather = idx != nullptr;
     const int64_t n_keys = gather ? n_idx : d->n_prefix;
     SplitArgs a;
@@ -164,6 +167,9 @@ int run_split(const tsw_attn_desc* d, const void* q, const void* k, const void* 
     a.n_splits = n_splits;
     a.scale_log2 = d->scale * kLog2e;
     a.B = 1;
+    a.root_s = root_s;
+    a.root_stride = root_stride;
+    a.root_clear = root_clear;
 
     tsw::MfmaConfig cfg;
     if (use_mfma(d, n_keys, &cfg)) {
@@ -172,9 +178,10 @@ int run_split(const tsw_attn_desc* d, const void* q, const void* k, const void* 
         if (gather && a.chunk_keys > tsw::kGatherChunkMax) return TSW_EUNSUPPORTED;
         if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v) & 15) return TSW_EINVAL;
         if (d->kv_head_stride % 8) return TSW_EINVAL;
-        return hip_status(tsw::launch_split_mfma(cfg, gather ? tsw::kModeGather : tsw::kModeContig, a, d->Hkv,
-                                                 stream));
+        const int mode = gather ? tsw::kModeGather : (root_s ? tsw::kModeContigRoot : tsw::kModeContig);
+        return hip_status(tsw::launch_split_mfma(cfg, mode, a, d->Hkv, stream));
     }
+    if (root_s) return TSW_EUNSUPPORTED;
     a.chunk_keys = cdiv(cdiv(n_keys, n_splits), tsw::kValuTile) * tsw::kValuTile;
     return hip_status(tsw::launch_split_valu(d->dtype, d->d, gather, a, d->Hkv, stream));
 }
@@ -305,6 +312,52 @@ int plan_paged(const tsw_paged_desc* d, const int64_t* n_prefix, const tsw::Mfma
 }
 
 // Partials of a paged call: every split holds its own sequence's T x Hq rows.
+// Checks shared by the selection entry points (after check_desc).
+int check_select(const tsw_attn_desc* d, const void* k, int64_t n_keep, int64_t n_idx, const int32_t* idx) {
+    if (d->Hq > tsw::kSelectMaxHeads) return TSW_EUNSUPPORTED;
+    if (d->n_prefix > INT32_MAX) return TSW_EUNSUPPORTED;
+    if (n_keep < 0 || n_idx < 0) return TSW_EBADINDEX;
+    if (!k) return TSW_EINVAL;
+    const int64_t n_out = n_idx < d->n_prefix ? n_idx : d->n_prefix;
+    if (n_out > 0 && !idx) return TSW_EINVAL;
+    const int esz = d->dtype == TSW_DTYPE_F32 ? 4 : 2;
+    if ((uintptr_t)k & 15) return TSW_EINVAL;
+    if ((d->kv_head_stride * esz) % 16) return TSW_EINVAL;
+    return TSW_OK;
+}
+
+size_t select_ws_bytes(int64_t n_prefix) {
+    const size_t b = align256((size_t)n_prefix * sizeof(float)) + align256(tsw::select_scratch_bytes(n_prefix));
+    return b < 256 ? 256 : b;
+}
+
+// Verification with selection: the split partials, the root-row scores
+// (matrix-core path: Hq rows of root_stride floats), then the selection's
+// own workspace.
+struct VsLayout {
+    int32_t n_splits;
+    bool root;
+    int64_t root_stride;
+    size_t off_root, off_sel, total;
+};
+
+int vs_layout(const tsw_attn_desc* d, VsLayout* L) {
+    int cus = 0;
+    int rc = device_cus(&cus);
+    if (rc != TSW_OK) return rc;
+    rc = plan(d, d->n_prefix, false, cus, &L->n_splits);
+    if (rc != TSW_OK) return rc;
+    tsw::MfmaConfig cfg;
+    // the kernel writes root scores for head groups of up to 16 (block 0)
+    L->root = use_mfma(d, d->n_prefix, &cfg) && d->Hq / d->Hkv <= 16;
+    L->root_stride = (d->n_prefix + 3) & ~(int64_t)3;
+    L->off_root = ws_bytes_for(d, L->n_splits);
+    const size_t root_bytes = L->root ? align256((size_t)d->Hq * L->root_stride * sizeof(float)) : 0;
+    L->off_sel = L->off_root + root_bytes;
+    L->total = L->off_sel + select_ws_bytes(d->n_prefix);
+    return TSW_OK;
+}
+
 size_t ws_bytes_paged(const tsw_paged_desc* d, int32_t total_splits) {
     const size_t rows = (size_t)d->T * d->Hq;
     return align256((size_t)total_splits * rows * d->d * sizeof(float)) +
@@ -506,8 +559,7 @@ int tsw_tree_attn_verify_paged(const tsw_paged_desc* desc, const void* q, const 
 
 int tsw_select_workspace_size(int64_t n_prefix, size_t* bytes) {
     if (!bytes || n_prefix < 0 || n_prefix > INT32_MAX) return TSW_EINVAL;
-    *bytes = align256((size_t)n_prefix * sizeof(float)) + align256(tsw::select_scratch_bytes(n_prefix));
-    if (*bytes < 256) *bytes = 256;
+    *bytes = select_ws_bytes(n_prefix);
     return TSW_OK;
 }
 
@@ -516,15 +568,10 @@ int tsw_select_partial(const tsw_attn_desc* desc, const void* q, const void* k, 
                        tsw_stream_t stream) {
     int rc = check_desc(desc);
     if (rc != TSW_OK) return rc;
-    if (desc->Hq > tsw::kSelectMaxHeads) return TSW_EUNSUPPORTED;
-    if (desc->n_prefix > INT32_MAX) return TSW_EUNSUPPORTED;
-    if (n_keep < 0 || n_idx < 0) return TSW_EBADINDEX;
-    if (!q || !k || !lse) return TSW_EINVAL;
+    rc = check_select(desc, k, n_keep, n_idx, idx);
+    if (rc != TSW_OK) return rc;
+    if (!q || !lse) return TSW_EINVAL;
     const int64_t n_out = n_idx < desc->n_prefix ? n_idx : desc->n_prefix;
-    if (n_out > 0 && !idx) return TSW_EINVAL;
-    const int esz = desc->dtype == TSW_DTYPE_F32 ? 4 : 2;
-    if ((uintptr_t)k & 15) return TSW_EINVAL;
-    if ((desc->kv_head_stride * esz) % 16) return TSW_EINVAL;
     if (!workspace) return TSW_EINVAL;
     if ((uintptr_t)workspace & 255) return TSW_EINVAL;
     const size_t imp_bytes = align256((size_t)desc->n_prefix * sizeof(float));
@@ -548,6 +595,79 @@ int tsw_select_partial(const tsw_attn_desc* desc, const void* q, const void* k, 
     if (rc != TSW_OK || n_out == 0) return rc;
     const int64_t keep = n_keep < n_out ? n_keep : n_out;
     return hip_status(tsw::launch_select(imp, desc->n_prefix, keep, n_out, idx, scratch, (hipStream_t)stream));
+}
+
+int tsw_verify_select_workspace_size(const tsw_attn_desc* desc, size_t* bytes) {
+    if (!bytes) return TSW_EINVAL;
+    int rc = check_desc(desc);
+    if (rc != TSW_OK) return rc;
+    if (desc->n_prefix > INT32_MAX) return TSW_EUNSUPPORTED;
+    VsLayout L;
+    rc = vs_layout(desc, &L);
+    if (rc != TSW_OK) return rc;
+    *bytes = L.total;
+    return TSW_OK;
+}
+
+int tsw_tree_attn_verify_select(const tsw_attn_desc* desc, const void* q, const void* k, const void* v,
+                                const int32_t* parent, float* o, float* lse, int64_t n_keep, int64_t n_idx,
+                                int32_t* idx, float* importance, void* workspace, size_t workspace_bytes,
+                                tsw_stream_t stream) {
+    int rc = check_common(desc, q, k, v, parent, o, lse);
+    if (rc != TSW_OK) return rc;
+    rc = check_select(desc, k, n_keep, n_idx, idx);
+    if (rc != TSW_OK) return rc;
+    if (!workspace || ((uintptr_t)workspace & 255)) return TSW_EINVAL;
+    VsLayout L;
+    rc = vs_layout(desc, &L);
+    if (rc != TSW_OK) return rc;
+    if (workspace_bytes < L.total) return TSW_ENOSPACE;
+    const size_t rows = (size_t)desc->T * desc->Hq;
+    char* ws = (char*)workspace;
+    float* part_o = (float*)ws;
+    float* part_lse = (float*)(ws + align256((size_t)L.n_splits * rows * desc->d * sizeof(float)));
+    float* root_s = L.root ? (float*)(ws + L.off_root) : nullptr;
+    char* sel = ws + L.off_sel;
+    float* imp = importance ? importance : (float*)sel;
+    uint32_t* scratch = (uint32_t*)(sel + align256((size_t)desc->n_prefix * sizeof(float)));
+    hipStream_t st = (hipStream_t)stream;
+
+    // the split kernel zeroes the selection's digit totals (scratch[0..1024))
+    rc = run_split(desc, q, k, v, parent, nullptr, 0, L.n_splits, part_o, part_lse, st, root_s, L.root_stride,
+                   L.root ? scratch : nullptr);
+    if (rc != TSW_OK) return rc;
+    rc = hip_status(tsw::launch_lse_merge(L.n_splits, (int64_t)rows, desc->d, part_o, part_lse, o, lse, st));
+    if (rc != TSW_OK) return rc;
+
+    const int64_t n_out = n_idx < desc->n_prefix ? n_idx : desc->n_prefix;
+    const int64_t keep = n_keep < n_out ? n_keep : n_out;
+    if (!L.root) {
+        // vector-ALU verification: importance from K as in tsw_select_partial
+        tsw::SelectArgs a;
+        memset(&a, 0, sizeof a);
+        a.q = q;
+        a.k = k;
+        a.lse = lse;
+        a.n_prefix = desc->n_prefix;
+        a.kv_head_stride = desc->kv_head_stride;
+        a.Hq = desc->Hq;
+        a.Hkv = desc->Hkv;
+        a.G = desc->Hq / desc->Hkv;
+        a.d = desc->d;
+        a.dtype = desc->dtype == TSW_DTYPE_F32 ? 0 : 1;
+        a.scale = desc->scale;
+        rc = hip_status(tsw::launch_importance(a, imp, st));
+        if (rc != TSW_OK || n_out == 0) return rc;
+        return hip_status(tsw::launch_select(imp, desc->n_prefix, keep, n_out, idx, scratch, st));
+    }
+    const float c = desc->scale * kLog2e;
+    // importance, the kept positions and the first radix pass's counts, then
+    // the remaining passes
+    rc = hip_status(tsw::launch_importance_from_scores(root_s, L.root_stride, lse, desc->Hq, desc->n_prefix, c,
+                                                       keep, imp, n_out > 0 ? scratch : nullptr, idx, st));
+    if (rc != TSW_OK || n_out == 0) return rc;
+    if (rc != TSW_OK) return rc;
+    return hip_status(tsw::launch_select_passes(imp, desc->n_prefix, keep, n_out, idx, scratch, 1, st));
 }
 
 const char* tsw_status_str(int status) {

@@ -11,7 +11,9 @@ namespace tsw {
 // How the split kernels find a key's K/V row: the cache position itself
 // (contiguous), through an index list (gather, the draft pass), or through
 // a per-sequence block table into a page pool (paged batch).
-enum { kModeContig = 0, kModeGather = 1, kModePaged = 2 };
+// Key layouts of the split kernel; kModeContigRoot is the contiguous layout
+// that also writes the root row's scores (SplitArgs::root_s).
+enum { kModeContig = 0, kModeGather = 1, kModePaged = 2, kModeContigRoot = 3 };
 
 // Everything a split kernel needs, passed by value as the kernel argument.
 // The tree mask travels here (one 64-bit word per node) so that no device
@@ -40,6 +42,12 @@ struct SplitArgs {
     // splits of sequence b are grid x in [seg_base[b], seg_base[b+1]), each
     // ceil(n / splits) keys rounded up to whole tiles, but the last
     int32_t seg_base[65];
+    // kModeContigRoot (Hq / Hkv <= 16): root_s[h * root_stride + p] =
+    // dot(q[0][h], k[g(h)][p]) (unscaled) for every committed position
+    // p < n_prefix
+    float* root_s;
+    int64_t root_stride;     // a multiple of 4
+    uint32_t* root_clear;    // kModeContigRoot: 1024 words zeroed by work-group (0, 0), or nullptr
 };
 
 // Partial rows grouped by sequence for the merge: sequence s owns splits
@@ -121,6 +129,15 @@ constexpr int64_t kSelBlock = 4096;    // candidates per selection work-group
 size_t select_scratch_bytes(int64_t n_prefix);
 hipError_t launch_select(const float* imp, int64_t n_prefix, int64_t n_keep, int64_t n_out, int32_t* idx,
                          uint32_t* scratch, hipStream_t stream);
+hipError_t launch_select_keep(int64_t n_keep, int32_t* idx, uint32_t* scratch, hipStream_t stream);
+// passes first_pass..3 (the earlier passes' totals already in scratch), flags, write
+hipError_t launch_select_passes(const float* imp, int64_t n_prefix, int64_t n_keep, int64_t n_out, int32_t* idx,
+                                uint32_t* scratch, int first_pass, hipStream_t stream);
+// Writes imp and idx[0..n_keep); totals: nullptr, or the scratch's digit
+// totals (already zero) to count the first pass's candidates p >= n_keep into
+hipError_t launch_importance_from_scores(const float* root_s, int64_t stride, const float* lse, int Hq,
+                                         int64_t n_prefix, float c, int64_t n_keep, float* imp, uint32_t* totals,
+                                         int32_t* idx, hipStream_t stream);
 
 // Key tile of the vector-ALU kernel and its query rows per work-group.
 constexpr int kValuTile = 64;

@@ -295,10 +295,33 @@ __device__ __forceinline__ void pv_block(const bf16x8& pb, const bf16x8 (&vop)[8
     for (int db = 0; db < 8; ++db) ob[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pb, vop[db], ob[db], 0, 0, 0);
 }
 
+// Root-row scores (node 0's query heads: rows r < G <= 16, all in block 0
+// of row group 0), lane li holding row li and four consecutive keys per key
+// half.  Prefix keys only; in a masked tile only those before the slice end.
+template <class S, bool MASKED>
+__device__ __forceinline__ void emit_root(const SplitArgs& a, const Ctx& cx, int tt, const f32x4 (&sc)[2]) {
+    if (cx.rg != 0) return;                          // uniform
+    if (MASKED && tt >= cx.n_pre_tiles) return;      // the tree's own rows
+    if (cx.li >= a.G) return;
+    float* dst = a.root_s + (size_t)(cx.g * a.G + cx.li) * a.root_stride +
+                 (cx.c0 + (int64_t)tt * S::TK + cx.ks * 32 + 4 * cx.lj);
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+        if constexpr (!MASKED) {
+            *(f32x4*)(dst + kb * 16) = sc[kb];
+        } else {
+            const int64_t key = cx.c0 + (int64_t)tt * S::TK + cx.ks * 32 + kb * 16 + 4 * cx.lj;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                if (key + i < cx.c1) dst[kb * 16 + i] = sc[kb][i];
+        }
+    }
+}
+
 // One key tile for a wave owning NBA query blocks: Q K of block b+1 is
 // issued next to the exponentials of block b (independent), then P V of
 // block b.  SHIFT subtracts the row maxima m (exact pass).
-template <class S, int NBA, bool MASKED, bool SHIFT>
+template <class S, int NBA, bool MASKED, bool SHIFT, bool EMIT>
 __device__ __forceinline__ void tile_pv(const SplitArgs& a, const Ctx& cx, int tt, float c, const bf16x8 (&kop)[2][4],
                                         const bf16x8 (&vop)[8], const bf16x8 (&qop)[NBA][4], const float (&m)[NBA],
                                         float (&l)[NBA], f32x4 (&o)[NBA][8]) {
@@ -311,6 +334,8 @@ __device__ __forceinline__ void tile_pv(const SplitArgs& a, const Ctx& cx, int t
             s_init<S, MASKED>(a, cx, tt, b + 1, sc[(b + 1) & 1]);
             qk_block(kop, qop[b + 1], sc[(b + 1) & 1]);
         }
+        if constexpr (EMIT)
+            if (b == 0) emit_root<S, MASKED>(a, cx, tt, sc[0]);
         bf16x8 pb;
         // a wave whose key sub-tiles held no visible key for a row has m = -inf
         softmax_block<SHIFT>(sc[b & 1], c, (SHIFT && m[b] != -INFINITY) ? m[b] : 0.0f, l[b], pb);
@@ -323,7 +348,7 @@ __device__ __forceinline__ void tile_pv(const SplitArgs& a, const Ctx& cx, int t
 // exponentials of all blocks, then P V one V column block at a time, so only
 // a step's K operands and one V operand are live.  The other wave on the
 // SIMD fills the matrix pipe while this one exponentiates.
-template <class S, int NBA, bool MASKED, bool SHIFT>
+template <class S, int NBA, bool MASKED, bool SHIFT, bool EMIT>
 __device__ __forceinline__ void tile_pv_shared(const SplitArgs& a, const Ctx& cx, int tt, float c, const char* Ks,
                                                const char* Vs, const bf16x8 (&qop)[NBA][4], const float (&m)[NBA],
                                                float (&l)[NBA], f32x4 (&o)[NBA][8]) {
@@ -343,6 +368,7 @@ __device__ __forceinline__ void tile_pv_shared(const SplitArgs& a, const Ctx& cx
                 sc[b][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qop[b][s], sc[b][kb], 0, 0, 0);
         }
     }
+    if constexpr (EMIT) emit_root<S, MASKED>(a, cx, tt, sc[0]);
     bf16x8 pb[NBA];
 #pragma unroll
     for (int b = 0; b < NBA; ++b)
@@ -387,7 +413,7 @@ __device__ __forceinline__ void tile_max(const SplitArgs& a, const Ctx& cx, int 
 }
 
 // The work of one wavefront owning NBA query blocks.
-template <class S, int LAYOUT, int NBA>
+template <class S, int LAYOUT, int NBA, bool EMIT>
 __device__ __forceinline__ void run_wave(const SplitArgs& a, const Ctx& cx) {
     constexpr int STAGES = S::STAGES;
     const float c = a.scale_log2;
@@ -464,12 +490,14 @@ __device__ __forceinline__ void run_wave(const SplitArgs& a, const Ctx& cx) {
                 load_k<S>(Ks, cx, kop);
                 tile_max<S, NBA, MASKED>(a, cx, t, c, kop, qop, m_run);
             } else if constexpr (S::WAVES == 8) {
-                tile_pv_shared<S, NBA, MASKED, MODE == EXACT>(a, cx, t, c, Ks, Ks + S::TK * S::ROWB, qop, m_run,
-                                                              l_run, o);
+                tile_pv_shared<S, NBA, MASKED, MODE == EXACT, EMIT && MODE == FAST>(a, cx, t, c, Ks,
+                                                                                   Ks + S::TK * S::ROWB, qop,
+                                                                                   m_run, l_run, o);
             } else {
                 load_k<S>(Ks, cx, kop);
                 load_v<S>(Ks + S::TK * S::ROWB, cx, vop);
-                tile_pv<S, NBA, MASKED, MODE == EXACT>(a, cx, t, c, kop, vop, qop, m_run, l_run, o);
+                tile_pv<S, NBA, MASKED, MODE == EXACT, EMIT && MODE == FAST>(a, cx, t, c, kop, vop, qop, m_run,
+                                                                            l_run, o);
             }
         };
         int t = 0;
@@ -619,8 +647,11 @@ __device__ __forceinline__ void run_wave(const SplitArgs& a, const Ctx& cx) {
     }
 }
 
-template <int W, int R, int NB, int MODE>
+template <int W, int R, int NB, int MODE_ARG>
 __global__ __launch_bounds__(W * 64, 1) void split_mfma(const SplitArgs a) {
+    // the root-score variant streams keys exactly as the contiguous layout
+    constexpr int MODE = MODE_ARG == kModeContigRoot ? kModeContig : MODE_ARG;
+    constexpr bool EMIT = MODE_ARG == kModeContigRoot;
     using S = Shape<W, R, NB, MODE>;
     constexpr int SMEM = S::SMEM;
     constexpr int MASK_OFF = (SMEM + S::POOL + 7) & ~7;
@@ -678,6 +709,11 @@ __global__ __launch_bounds__(W * 64, 1) void split_mfma(const SplitArgs a) {
     cx.mask_lds = mask_lds;
     // visible to all waves after the first barrier of the tile loop
     if (threadIdx.x < (unsigned)a.T) mask_lds[threadIdx.x] = a.mask[threadIdx.x];
+    // the root-score variant also zeroes the counters its consumer
+    // accumulates into (the kernel that runs before their first use)
+    if constexpr (EMIT)
+        if (a.root_clear && blockIdx.x == 0 && blockIdx.y == 0)
+            for (int i = threadIdx.x; i < 1024; i += W * 64) a.root_clear[i] = 0u;
     cx.pg0 = cx.tpg0 = 0;
     cx.npg = 0;
     if constexpr (MODE == kModeGather) {
@@ -704,10 +740,10 @@ __global__ __launch_bounds__(W * 64, 1) void split_mfma(const SplitArgs a) {
     const int nblk = (a.M + 15) >> 4;
     const int nb_act = (nblk - cx.rg + S::R - 1) / S::R;
     if constexpr (S::R == 1) {
-        run_wave<S, MODE, NB>(a, cx);
+        run_wave<S, MODE, NB, EMIT>(a, cx);
     } else {
-        if (nb_act >= NB) run_wave<S, MODE, NB>(a, cx);
-        else run_wave<S, MODE, NB - 1>(a, cx);
+        if (nb_act >= NB) run_wave<S, MODE, NB, EMIT>(a, cx);
+        else run_wave<S, MODE, NB - 1, EMIT>(a, cx);
     }
 }
 
@@ -719,6 +755,8 @@ hipError_t launch(int mode, const SplitArgs& a, int n_kv_heads, hipStream_t stre
         hipLaunchKernelGGL((split_mfma<W, R, NB, kModeGather>), grid, dim3(W * 64), 0, stream, a);
     else if (mode == kModePaged)
         hipLaunchKernelGGL((split_mfma<W, R, NB, kModePaged>), grid, dim3(W * 64), 0, stream, a);
+    else if (mode == kModeContigRoot)
+        hipLaunchKernelGGL((split_mfma<W, R, NB, kModeContigRoot>), grid, dim3(W * 64), 0, stream, a);
     else
         hipLaunchKernelGGL((split_mfma<W, R, NB, kModeContig>), grid, dim3(W * 64), 0, stream, a);
     return hipGetLastError();

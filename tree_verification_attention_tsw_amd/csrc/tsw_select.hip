@@ -18,6 +18,9 @@
 //                      formed in one fixed order, no atomics), a wavefront 16
 //                      keys at a time with lane (key, quarter of d).
 //   select_keep        the kept initial positions; clears the digit totals.
+//   importance_from_scores  the same importance from the root-row scores the
+//                      verification kernel wrote (K is not read again), with
+//                      the first radix pass's digit counts.
 //   select_count x4    radix selection of the r-th largest importance: four
 //                      8-bit passes over the float bits (which order
 //                      non-negative floats), digit counts summed into the
@@ -92,41 +95,56 @@ __global__ __launch_bounds__(256) void importance_kernel(const SelectArgs a, flo
 // Selection state after `passes` radix passes, derived from the digit totals
 // of those passes (every work-group derives the same values).  The digit of
 // a pass is the one whose count, added to the counts of the larger digits,
-// first reaches the number still needed: a suffix scan over the 256 digits,
-// one digit per thread.
+// first reaches the number still needed.  Wavefront 0 does it: lane l holds
+// digits 4l..4l+3, a shuffle suffix scan over the lanes gives each lane the
+// count above its digits, and the one lane whose range holds the crossing
+// names the digit.  One barrier publishes the state.
 struct SelState {
     uint32_t prefix, mask, need;
 };
 
 __device__ SelState derive_state(const uint32_t* __restrict__ totals, int passes, uint32_t r,
-                                 uint32_t* sfx /* LDS [256] */, uint32_t* bcast /* LDS [2] */) {
-    SelState st{0u, 0u, r};
-    const int t = threadIdx.x;
-    uint32_t mine[4];
+                                 uint32_t* out /* LDS [3] */) {
+    if (threadIdx.x < 64) {
+        const int l = threadIdx.x;
+        uint4 v[4];
 #pragma unroll
-    for (int p = 0; p < 4; ++p) mine[p] = p < passes ? totals[p * 256 + t] : 0u;   // one round trip
-    for (int p = 0; p < passes; ++p) {
-        // inclusive suffix sums: sfx[d] = sum of totals[d' >= d]
-        sfx[t] = mine[p];
-        __syncthreads();
-        for (int off = 1; off < 256; off <<= 1) {
-            const uint32_t y = t + off < 256 ? sfx[t + off] : 0u;
-            __syncthreads();
-            sfx[t] += y;
-            __syncthreads();
+        for (int p = 0; p < 4; ++p)
+            v[p] = p < passes ? *(const uint4*)(totals + p * 256 + 4 * l) : uint4{0u, 0u, 0u, 0u};
+        uint32_t prefix = 0u, mask = 0u, need = r;
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            if (p >= passes) break;
+            const uint32_t mine = v[p].x + v[p].y + v[p].z + v[p].w;
+            uint32_t sfx = mine;                     // sum over lanes >= l
+#pragma unroll
+            for (int off = 1; off < 64; off <<= 1) {
+                const uint32_t y = __shfl_down(sfx, off);
+                if (l + off < 64) sfx += y;
+            }
+            // counts above digits 4l+3, 4l+2, 4l+1, 4l
+            const uint32_t a3 = sfx - mine, a2 = a3 + v[p].w, a1 = a2 + v[p].z, a0 = a1 + v[p].y;
+            int d = -1;
+            uint32_t rest = 0u;
+            if (a3 < need && need <= a2) { d = 4 * l + 3; rest = need - a3; }
+            else if (a2 < need && need <= a1) { d = 4 * l + 2; rest = need - a2; }
+            else if (a1 < need && need <= a0) { d = 4 * l + 1; rest = need - a1; }
+            else if (a0 < need && need <= a0 + v[p].x) { d = 4 * l; rest = need - a0; }
+            const uint64_t found = __builtin_amdgcn_ballot_w64(d >= 0);
+            const int src = found ? __builtin_ctzll(found) : 0;   // exactly one lane when need <= candidates
+            const uint32_t dig = (uint32_t)__shfl(d, src) & 255u;
+            need = (uint32_t)__shfl(rest, src);
+            prefix |= dig << (24 - 8 * p);
+            mask |= 255u << (24 - 8 * p);
         }
-        const uint32_t above = sfx[t] - mine[p];     // keys in larger digits
-        if (above < st.need && st.need <= sfx[t]) {
-            bcast[0] = (uint32_t)t;
-            bcast[1] = st.need - above;              // still to take inside this digit
+        if (l == 0) {
+            out[0] = prefix;
+            out[1] = mask;
+            out[2] = need;
         }
-        __syncthreads();
-        st.prefix |= bcast[0] << (24 - 8 * p);
-        st.mask |= 255u << (24 - 8 * p);
-        st.need = bcast[1];
-        __syncthreads();
     }
-    return st;
+    __syncthreads();
+    return SelState{out[0], out[1], out[2]};
 }
 
 // The always-kept initial positions; also clears the digit totals of the
@@ -139,36 +157,93 @@ __global__ __launch_bounds__(256) void select_keep(int64_t n_keep, int32_t* __re
         for (int j = threadIdx.x; j < 4 * 256; j += 256) totals[j] = 0u;
 }
 
+// Adds the hitting lanes' digits d to a wave's LDS table: one add when they
+// all share a digit (values are often concentrated in a few high digits),
+// else one LDS atomic per lane.
+__device__ __forceinline__ void wave_count(uint32_t* wt, uint32_t d, bool hit) {
+    const uint64_t hits = __builtin_amdgcn_ballot_w64(hit);
+    if (hits == 0) return;
+    const uint32_t d_first = __shfl(d, __builtin_ctzll(hits));       // the first hitting lane's digit
+    const bool same = __builtin_amdgcn_ballot_w64(hit && d != d_first) == 0;
+    if (same) {
+        if ((threadIdx.x & 63) == 0) wt[d_first] += (uint32_t)__builtin_popcountll(hits);
+    } else if (hit) {
+        atomicAdd(&wt[d], 1u);
+    }
+}
+
+// Importance from the root-row scores the verification kernel wrote:
+// imp[p] = sum_h 2^(c * s[h][p] - log2(e) * lse[h]) over the query heads in
+// order (c = scale * log2(e)), four keys per thread; also idx[p] = p for the
+// kept positions p < n_keep.  With totals != nullptr it adds the first radix
+// pass's digit counts of the candidates p >= n_keep (the totals were cleared
+// by the verification kernel).
+__global__ __launch_bounds__(256) void importance_from_scores(const float* __restrict__ root_s, int64_t stride,
+                                                              const float* __restrict__ lse, int Hq,
+                                                              int64_t n_prefix, float c, int64_t n_keep,
+                                                              float* __restrict__ imp,
+                                                              uint32_t* __restrict__ totals,
+                                                              int32_t* __restrict__ idx) {
+    __shared__ float ls[kSelectMaxHeads];
+    __shared__ uint32_t wt[4][256];
+    const int t = threadIdx.x, w = t >> 6;
+    for (int i = t; i < Hq; i += 256) ls[i] = lse[i] * kLog2e;
+    for (int i = t; i < 4 * 256; i += 256) (&wt[0][0])[i] = 0;
+    __syncthreads();
+    // four keys per thread (16-byte loads), eight heads' loads in flight
+    const int64_t p0 = ((int64_t)blockIdx.x * 256 + t) * 4;
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+    if (p0 + 4 <= n_prefix) {
+        const float* src = root_s + p0;
+#pragma unroll 8
+        for (int h = 0; h < Hq; ++h) {
+            const f32x4 x = *(const f32x4*)(src + (size_t)h * stride);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[i] += exp2_fast(fmaf(x[i], c, -ls[h]));
+        }
+    } else if (p0 < n_prefix) {
+        for (int h = 0; h < Hq; ++h)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                if (p0 + i < n_prefix) acc[i] += exp2_fast(fmaf(root_s[(size_t)h * stride + p0 + i], c, -ls[h]));
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        if (p0 + i < n_prefix) imp[p0 + i] = acc[i];
+        if (p0 + i < n_keep) idx[p0 + i] = (int32_t)(p0 + i);     // the kept initial positions
+    }
+    if (totals == nullptr) return;                   // uniform
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        wave_count(wt[w], __float_as_uint(acc[i]) >> 24, p0 + i >= n_keep && p0 + i < n_prefix);
+    __syncthreads();
+    const uint32_t cnt = wt[0][t] + wt[1][t] + wt[2][t] + wt[3][t];
+    if (cnt) atomicAdd(&totals[t], cnt);
+}
+
 // Radix pass `pass` (8-bit digit, high to low) over block blockIdx.x's
 // kSelBlock candidates: digit counts of the keys that match the state so
-// far, added to the pass's totals.  Per-wave LDS tables; a wave whose hitting
-// lanes share a digit adds once (values are often concentrated in the high
-// digits).
+// far, added to the pass's totals (per-wave LDS tables first).
 __global__ __launch_bounds__(256) void select_count(const uint32_t* __restrict__ key, int64_t m, uint32_t r, int pass,
                                                     uint32_t* __restrict__ totals) {
+    constexpr int RUN = kSelBlock / 256;
     __shared__ uint32_t wt[4][256];
-    __shared__ uint32_t sfx[256];
-    __shared__ uint32_t bcast[2];
+    __shared__ uint32_t st_lds[3];
     const int t = threadIdx.x, w = t >> 6;
-    for (int i = t; i < 4 * 256; i += 256) (&wt[0][0])[i] = 0;
-    const SelState st = derive_state(totals, pass, r, sfx, bcast);
-    const int shift = 24 - 8 * pass;
     const int64_t base = (int64_t)blockIdx.x * kSelBlock;
-    for (int j = 0; j < kSelBlock / 256; ++j) {
+    uint32_t k[RUN];                                 // all loads in flight before the state is known
+#pragma unroll
+    for (int j = 0; j < RUN; ++j) {
         const int64_t i = base + j * 256 + t;
-        const bool live = i < m;
-        const uint32_t k = live ? key[i] : 0u;
-        const bool hit = live && (k & st.mask) == st.prefix;
-        const uint32_t d = (k >> shift) & 255u;
-        const uint64_t hits = __builtin_amdgcn_ballot_w64(hit);
-        if (hits == 0) continue;
-        const uint32_t d_first = __shfl(d, __builtin_ctzll(hits));       // the first hitting lane's digit
-        const bool same = __builtin_amdgcn_ballot_w64(hit && d != d_first) == 0;
-        if (same) {
-            if ((t & 63) == 0) wt[w][d_first] += (uint32_t)__builtin_popcountll(hits);
-        } else if (hit) {
-            atomicAdd(&wt[w][d], 1u);
-        }
+        k[j] = i < m ? key[i] : 0u;
+    }
+    for (int i = t; i < 4 * 256; i += 256) (&wt[0][0])[i] = 0;
+    const SelState st = derive_state(totals, pass, r, st_lds);
+    const int shift = 24 - 8 * pass;
+#pragma unroll
+    for (int j = 0; j < RUN; ++j) {
+        const bool hit = base + j * 256 + t < m && (k[j] & st.mask) == st.prefix;
+        wave_count(wt[w], (k[j] >> shift) & 255u, hit);
     }
     __syncthreads();
     const uint32_t c = wt[0][t] + wt[1][t] + wt[2][t] + wt[3][t];
@@ -180,20 +255,24 @@ __global__ __launch_bounds__(256) void select_count(const uint32_t* __restrict__
 __global__ __launch_bounds__(256) void select_flags(const uint32_t* __restrict__ key, int64_t m, uint32_t r,
                                                     const uint32_t* __restrict__ totals,
                                                     uint32_t* __restrict__ counts) {
-    __shared__ uint32_t sfx[256];
-    __shared__ uint32_t bcast[2];
+    constexpr int RUN = kSelBlock / 256;
+    __shared__ uint32_t st_lds[3];
     __shared__ uint32_t red[2][4];
     const int t = threadIdx.x;
-    const SelState st = derive_state(totals, 4, r, sfx, bcast);
     const int64_t base = (int64_t)blockIdx.x * kSelBlock;
-    uint32_t gt = 0, eq = 0;
-    for (int j = 0; j < kSelBlock / 256; ++j) {
+    uint32_t k[RUN];
+#pragma unroll
+    for (int j = 0; j < RUN; ++j) {
         const int64_t i = base + j * 256 + t;
-        if (i < m) {
-            const uint32_t k = key[i];
-            gt += k > st.prefix;
-            eq += k == st.prefix;
-        }
+        k[j] = i < m ? key[i] : 0u;
+    }
+    const SelState st = derive_state(totals, 4, r, st_lds);
+    uint32_t gt = 0, eq = 0;
+#pragma unroll
+    for (int j = 0; j < RUN; ++j) {
+        const bool live = base + j * 256 + t < m;
+        gt += live && k[j] > st.prefix;
+        eq += live && k[j] == st.prefix;
     }
     for (int off = 32; off >= 1; off >>= 1) {
         gt += __shfl_xor(gt, off);
@@ -218,16 +297,19 @@ __global__ __launch_bounds__(256) void select_write(const uint32_t* __restrict__
                                                     const uint32_t* __restrict__ counts, int64_t n_keep,
                                                     int32_t* __restrict__ idx) {
     constexpr int RUN = kSelBlock / 256;
-    __shared__ uint32_t sfx[256];
-    __shared__ uint32_t bcast[2];
-    __shared__ uint32_t scan[2][256];
+    __shared__ uint32_t st_lds[3];
+    __shared__ uint32_t wsum[2][4];
     __shared__ uint32_t blk_off[2];
-    const int t = threadIdx.x;
-    const SelState st = derive_state(totals, 4, r, sfx, bcast);
+    const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+    const int64_t lo = (int64_t)blockIdx.x * kSelBlock + (int64_t)t * RUN;
+    uint32_t k[RUN];
+#pragma unroll
+    for (int j = 0; j < RUN; ++j) k[j] = lo + j < m ? key[lo + j] : 0u;
+    const SelState st = derive_state(totals, 4, r, st_lds);
     // counts of the earlier blocks, one block per thread, summed in a wave
-    if (t < 64) {
+    if (t >= 192) {
         uint32_t g = 0, e = 0;
-        for (int blk = t; blk < (int)blockIdx.x; blk += 64) {
+        for (int blk = t - 192; blk < (int)blockIdx.x; blk += 64) {
             g += counts[2 * blk];
             e += counts[2 * blk + 1];
         }
@@ -235,35 +317,40 @@ __global__ __launch_bounds__(256) void select_write(const uint32_t* __restrict__
             g += __shfl_xor(g, off);
             e += __shfl_xor(e, off);
         }
-        if (t == 0) {
+        if (t == 192) {
             blk_off[0] = g;
             blk_off[1] = e;
         }
     }
-    const int64_t lo = (int64_t)blockIdx.x * kSelBlock + (int64_t)t * RUN;
-    uint32_t k[RUN];
     uint32_t gt = 0, eq = 0;
 #pragma unroll
     for (int j = 0; j < RUN; ++j) {
         const bool live = lo + j < m;
-        k[j] = live ? key[lo + j] : 0u;
         gt += live && k[j] > st.prefix;
         eq += live && k[j] == st.prefix;
     }
-    // exclusive scans of the per-thread counts across the block
-    scan[0][t] = gt;
-    scan[1][t] = eq;
-    __syncthreads();
-    for (int off = 1; off < 256; off <<= 1) {
-        const uint32_t a0 = t >= off ? scan[0][t - off] : 0u;
-        const uint32_t a1 = t >= off ? scan[1][t - off] : 0u;
-        __syncthreads();
-        scan[0][t] += a0;
-        scan[1][t] += a1;
-        __syncthreads();
+    // exclusive scans of the per-thread counts across the block: inclusive
+    // shuffle scans in each wave, then the totals of the earlier waves
+    uint32_t sg = gt, se = eq;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const uint32_t yg = __shfl_up(sg, off), ye = __shfl_up(se, off);
+        if (lane >= off) {
+            sg += yg;
+            se += ye;
+        }
     }
-    uint32_t gt_before = blk_off[0] + scan[0][t] - gt;
-    uint32_t eq_before = blk_off[1] + scan[1][t] - eq;
+    if (lane == 63) {
+        wsum[0][w] = sg;
+        wsum[1][w] = se;
+    }
+    __syncthreads();
+    uint32_t gt_before = blk_off[0] + sg - gt;
+    uint32_t eq_before = blk_off[1] + se - eq;
+    for (int v = 0; v < w; ++v) {
+        gt_before += wsum[0][v];
+        eq_before += wsum[1][v];
+    }
 #pragma unroll
     for (int j = 0; j < RUN; ++j) {
         if (lo + j >= m) break;
@@ -297,20 +384,23 @@ size_t select_scratch_bytes(int64_t n_prefix) {
     return (size_t)(4 * 256 + 2 * n_blocks) * sizeof(uint32_t);
 }
 
-hipError_t launch_select(const float* imp, int64_t n_prefix, int64_t n_keep, int64_t n_out, int32_t* idx,
-                         uint32_t* scratch, hipStream_t stream) {
+hipError_t launch_select_keep(int64_t n_keep, int32_t* idx, uint32_t* scratch, hipStream_t stream) {
+    hipLaunchKernelGGL(select_keep, dim3((unsigned)(n_keep > 0 ? (n_keep + 255) / 256 : 1)), dim3(256), 0, stream,
+                       n_keep, idx, scratch);
+    return hipGetLastError();
+}
+
+hipError_t launch_select_passes(const float* imp, int64_t n_prefix, int64_t n_keep, int64_t n_out, int32_t* idx,
+                                uint32_t* scratch, int first_pass, hipStream_t stream) {
     uint32_t* totals = scratch;                     // [4][256] digit totals
     uint32_t* counts = scratch + 4 * 256;           // [n_blocks][2]
-    hipLaunchKernelGGL(select_keep, dim3((unsigned)(n_keep > 0 ? (n_keep + 255) / 256 : 1)), dim3(256), 0, stream,
-                       n_keep, idx, totals);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
     const int64_t m = n_prefix - n_keep;             // candidates
     const int64_t r = n_out - n_keep;                // to choose among them (r <= m)
     if (m <= 0 || r <= 0) return hipSuccess;
     const int n_blocks = (int)((m + kSelBlock - 1) / kSelBlock);
     const uint32_t* key = (const uint32_t*)(imp + n_keep);     // non-negative floats order as uint32
-    for (int pass = 0; pass < 4; ++pass) {
+    hipError_t e;
+    for (int pass = first_pass; pass < 4; ++pass) {
         hipLaunchKernelGGL(select_count, dim3(n_blocks), dim3(256), 0, stream, key, m, (uint32_t)r, pass, totals);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
@@ -320,6 +410,23 @@ hipError_t launch_select(const float* imp, int64_t n_prefix, int64_t n_keep, int
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(select_write, dim3(n_blocks), dim3(256), 0, stream, key, m, (uint32_t)r, totals, counts,
                        n_keep, idx);
+    return hipGetLastError();
+}
+
+hipError_t launch_select(const float* imp, int64_t n_prefix, int64_t n_keep, int64_t n_out, int32_t* idx,
+                         uint32_t* scratch, hipStream_t stream) {
+    const hipError_t e = launch_select_keep(n_keep, idx, scratch, stream);
+    if (e != hipSuccess) return e;
+    return launch_select_passes(imp, n_prefix, n_keep, n_out, idx, scratch, 0, stream);
+}
+
+hipError_t launch_importance_from_scores(const float* root_s, int64_t stride, const float* lse, int Hq,
+                                         int64_t n_prefix, float c, int64_t n_keep, float* imp, uint32_t* totals,
+                                         int32_t* idx, hipStream_t stream) {
+    if (n_prefix <= 0) return hipSuccess;
+    const unsigned grid = (unsigned)((n_prefix + 1023) / 1024);
+    hipLaunchKernelGGL(importance_from_scores, dim3(grid), dim3(256), 0, stream, root_s, stride, lse, Hq, n_prefix,
+                       c, n_keep, imp, totals, idx);
     return hipGetLastError();
 }
 

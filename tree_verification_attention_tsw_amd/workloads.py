@@ -220,10 +220,13 @@ class SelectWorkload:
     attn: str          # the verification workload whose q, k, lse feed it
     n_keep: int
     n_idx: int
+    with_verify: bool = False   # timed together with the verification that feeds it
 
 
 SELECT_WORKLOADS = {
     "select_gqa8b_100k": SelectWorkload("select_gqa8b_100k", attn="gqa8b_100k", n_keep=128, n_idx=4096),
+    "verify_select_gqa8b_100k": SelectWorkload("verify_select_gqa8b_100k", attn="gqa8b_100k", n_keep=128,
+                                               n_idx=4096, with_verify=True),
 }
 
 
