@@ -167,19 +167,19 @@ __global__ __launch_bounds__(256) void split_valu(const SplitArgs a) {
 // its own run of splits): lanes hold the split LSEs (64 at a time),
 // wave reductions give the row's LSE, and each lane accumulates d/64
 // consecutive columns over the splits with coalesced loads.  The partial
-// rows do not depend on the LSEs, so the first kMergeChunk of them are
-// loaded together with the LSEs: a row costs about one memory round trip.
-constexpr int kMergeChunk = 32;
+// rows do not depend on the LSEs, so the first CH of them are loaded
+// together with the LSEs: a row costs about one memory round trip.  CH (8,
+// 16 or 32) is the smallest chunk that holds the split count, so few loads
+// repeat a split past the end.
 
 // Output row r from the n_splits partial rows rr of blocks of `stride` rows
 // (part_o / part_lse point at the first split of the row's run).
-template <int D>
+template <int D, int CH>
 __device__ __forceinline__ void merge_row(int n_splits, int64_t stride, int64_t rr, int64_t r,
                                           const float* __restrict__ part_o,
                                           const float* __restrict__ part_lse, float* __restrict__ o,
                                           float* __restrict__ lse) {
     constexpr int PER = D / 64;
-    constexpr int CH = kMergeChunk;
     using VT = typename std::conditional<PER == 2, float2, float>::type;
     constexpr float kL2e = 1.44269504088896340736f;
     const int lane = threadIdx.x & 63;
@@ -248,17 +248,17 @@ __device__ __forceinline__ void merge_row(int n_splits, int64_t stride, int64_t 
 }
 
 // One sequence: n_splits blocks of n_rows rows.
-template <int D>
+template <int D, int CH>
 __global__ __launch_bounds__(256) void lse_merge(int n_splits, int64_t n_rows, const float* __restrict__ part_o,
                                                  const float* __restrict__ part_lse, float* __restrict__ o,
                                                  float* __restrict__ lse) {
     const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     if (r >= n_rows) return;
-    merge_row<D>(n_splits, n_rows, r, r, part_o, part_lse, o, lse);
+    merge_row<D, CH>(n_splits, n_rows, r, r, part_o, part_lse, o, lse);
 }
 
 // Several sequences, each with its own run of splits of rows_per_seg rows.
-template <int D>
+template <int D, int CH>
 __global__ __launch_bounds__(256) void lse_merge_segs(const MergeSegs segs, int64_t n_rows,
                                                       const float* __restrict__ part_o,
                                                       const float* __restrict__ part_lse, float* __restrict__ o,
@@ -268,7 +268,7 @@ __global__ __launch_bounds__(256) void lse_merge_segs(const MergeSegs segs, int6
     const int seg = (int)((uint32_t)r / (uint32_t)segs.rows_per_seg);
     const int64_t rr = r - (int64_t)seg * segs.rows_per_seg;
     const int64_t first = (int64_t)segs.base[seg] * segs.rows_per_seg;
-    merge_row<D>(segs.base[seg + 1] - segs.base[seg], segs.rows_per_seg, rr, r, part_o + first * D, part_lse + first,
+    merge_row<D, CH>(segs.base[seg + 1] - segs.base[seg], segs.rows_per_seg, rr, r, part_o + first * D, part_lse + first,
                  o, lse);
 }
 
@@ -330,7 +330,17 @@ hipError_t launch_lse_merge_segs(const MergeSegs& segs, int64_t n_rows, const fl
                                  const float* part_lse, float* o, float* lse, hipStream_t stream) {
     if (n_rows == 0) return hipSuccess;
     const dim3 grid((unsigned)((n_rows + 3) / 4));
-    hipLaunchKernelGGL(lse_merge_segs<128>, grid, dim3(256), 0, stream, segs, n_rows, part_o, part_lse, o, lse);
+    int most = 1;
+    for (int b = 0; b < segs.n_seg; ++b)
+        most = segs.base[b + 1] - segs.base[b] > most ? segs.base[b + 1] - segs.base[b] : most;
+    if (most <= 8)
+        hipLaunchKernelGGL((lse_merge_segs<128, 8>), grid, dim3(256), 0, stream, segs, n_rows, part_o, part_lse, o, lse);
+    else if (most <= 16)
+        hipLaunchKernelGGL((lse_merge_segs<128, 16>), grid, dim3(256), 0, stream, segs, n_rows, part_o, part_lse, o,
+                           lse);
+    else
+        hipLaunchKernelGGL((lse_merge_segs<128, 32>), grid, dim3(256), 0, stream, segs, n_rows, part_o, part_lse, o,
+                           lse);
     return hipGetLastError();
 }
 
@@ -339,10 +349,18 @@ hipError_t launch_lse_merge(int n_splits, int64_t n_rows, int d, const float* pa
     if (n_rows == 0) return hipSuccess;
     if (d == 128 || d == 64) {
         const dim3 grid((unsigned)((n_rows + 3) / 4));
-        if (d == 128)
-            hipLaunchKernelGGL(lse_merge<128>, grid, dim3(256), 0, stream, n_splits, n_rows, part_o, part_lse, o, lse);
-        else
-            hipLaunchKernelGGL(lse_merge<64>, grid, dim3(256), 0, stream, n_splits, n_rows, part_o, part_lse, o, lse);
+#define TSW_MERGE(D_, CH_) \
+    hipLaunchKernelGGL((lse_merge<D_, CH_>), grid, dim3(256), 0, stream, n_splits, n_rows, part_o, part_lse, o, lse)
+        if (d == 128) {
+            if (n_splits <= 8) TSW_MERGE(128, 8);
+            else if (n_splits <= 16) TSW_MERGE(128, 16);
+            else TSW_MERGE(128, 32);
+        } else {
+            if (n_splits <= 8) TSW_MERGE(64, 8);
+            else if (n_splits <= 16) TSW_MERGE(64, 16);
+            else TSW_MERGE(64, 32);
+        }
+#undef TSW_MERGE
         return hipGetLastError();
     }
     const int64_t n = n_rows * d;
