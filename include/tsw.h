@@ -275,6 +275,28 @@ int tsw_accept_greedy(const int32_t* parent, int32_t T, const void* logits, int6
                       int32_t logits_dtype, const int32_t* draft, int32_t* result, void* workspace,
                       size_t workspace_bytes, tsw_stream_t stream);
 
+/* Contextual penalty on the target logits of every tree node, in place,
+ * before tsw_accept_greedy ("TokenSwift - A framework for accelerating the
+ * generation of ultra-long text" (aiboss88), technical principles,
+ * contextual penalty strategy: recently generated tokens are penalised; the
+ * form and window are this library's reading, the usual repetition
+ * penalty).  Node t's window is the last `window` tokens of recent[0 ..
+ * n_recent) (the committed tokens, oldest first; the last one is the root's)
+ * followed by draft[] along the path from the root down to t (depth 1 ..
+ * depth(t)): what sequential generation had produced before predicting the
+ * token after t.  For every distinct id v in it with 0 <= v < vocab,
+ * logits[t][v] becomes l / theta when l > 0, else l * theta (float32
+ * arithmetic, correctly rounded; bfloat16 logits are widened and the result
+ * rounded to nearest even).  Other ids are ignored.
+ *   parent [T] int32   HOST, as for tsw_tree_attn_verify
+ *   logits [T][vocab]  device, float32 or bfloat16 (logits_dtype), modified
+ *   draft  [T] int32   device (draft[0] unused); recent [n_recent] int32 device
+ * window in 0 .. 8192, theta >= 1 and finite; window 0 or theta 1 launch
+ * nothing.  Errors: TSW_EINVAL, TSW_EBADTREE, TSW_EUNSUPPORTED, TSW_EHIP. */
+int tsw_context_penalty(const int32_t* parent, int32_t T, void* logits, int64_t vocab, int32_t logits_dtype,
+                        const int32_t* draft, const int32_t* recent, int64_t n_recent, int32_t window, float theta,
+                        tsw_stream_t stream);
+
 /* Moves the accepted path's K and V rows into place for n_layers caches:
  * for k = 1 .. L-1 the row at n_prefix + path[k] is copied to n_prefix + k
  * (row n_prefix + 0, the root, stays); the caller then commits

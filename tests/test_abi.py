@@ -279,3 +279,27 @@ def test_verify_select_argument_errors(L):
     assert call(desc=_desc(Hq=128, Hkv=8)) == EUNSUP
     assert call(desc=_desc(d=96)) == EUNSUP
     assert L.tsw_verify_select_workspace_size(ctypes.byref(_desc()), None) == EINVAL
+
+
+def test_penalty_argument_errors(L):
+    p = PARENT.ctypes.data_as(ctypes.c_void_p)
+
+    def call(parent=p, T=13, logits=FAKE, vocab=1000, dtype=0, draft=FAKE, recent=FAKE, n_recent=10, window=64,
+             theta=1.2):
+        return L.tsw_context_penalty(parent, T, logits, vocab, dtype, draft, recent, n_recent, window, theta, None)
+    assert call(window=-1) == EINVAL
+    assert call(window=8193) == EINVAL
+    assert call(theta=0.5) == EINVAL                      # would raise repeated tokens
+    assert call(theta=float("nan")) == EINVAL
+    assert call(theta=float("inf")) == EINVAL
+    assert call(n_recent=-1) == EINVAL
+    assert call(logits=None) == EINVAL
+    assert call(draft=None) == EINVAL
+    assert call(recent=None) == EINVAL
+    assert call(dtype=5) == EUNSUP
+    assert call(T=0) == EINVAL
+    bad = PARENT.copy()
+    bad[5] = 7
+    assert call(parent=bad.ctypes.data_as(ctypes.c_void_p)) == EBADTREE
+    assert call(window=0) == TSW_OK                       # nothing to do: no launch, no device needed
+    assert call(theta=1.0) == TSW_OK

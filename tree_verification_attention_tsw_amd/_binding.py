@@ -72,6 +72,7 @@ def lib():
     L.tsw_select_partial.argtypes = [D, vp, vp, vp, i64, i64, vp, vp, vp, sz, vp]
     L.tsw_verify_select_workspace_size.argtypes = [D, ctypes.POINTER(sz)]
     L.tsw_tree_attn_verify_select.argtypes = [D, vp, vp, vp, vp, vp, vp, i64, i64, vp, vp, vp, sz, vp]
+    L.tsw_context_penalty.argtypes = [vp, i32, vp, i64, i32, vp, vp, i64, i32, ctypes.c_float, vp]
     L.tsw_accept_workspace_size.argtypes = [i32, i64, ctypes.POINTER(sz)]
     L.tsw_accept_greedy.argtypes = [vp, i32, vp, i64, i32, vp, vp, vp, sz, vp]
     L.tsw_kv_compact.argtypes = [vp, vp, i32, i64, i32, i32, i32, i64, i64, i32, vp, vp]
@@ -355,6 +356,37 @@ def _accept_args(parent, logits, draft, result, workspace, stream):
     args = (_np_ptr(p), T, _dev_ptr(logits), vocab, _logits_dtype(logits), _dev_ptr(draft),
             _dev_ptr(result), _dev_ptr(workspace), workspace.numel(), st)
     return args, (p, result, workspace)
+
+
+def _penalty_args(parent, logits, draft, recent, window, theta, stream):
+    if logits.dim() != 2 or not logits.is_cuda or not logits.is_contiguous():
+        raise ValueError("logits must be a contiguous [T, vocab] GPU tensor")
+    T, vocab = logits.shape
+    for name, x in (("draft", draft), ("recent", recent)):
+        if x.dtype != torch.int32 or not x.is_cuda or not x.is_contiguous():
+            raise ValueError(name + " must be a contiguous int32 GPU tensor")
+    if draft.numel() != T:
+        raise ValueError("draft must have T entries")
+    p = _parent_arr(parent)
+    if p.shape[0] != T:
+        raise ValueError("parent must have T entries")
+    st = ctypes.c_void_p(stream.cuda_stream if stream is not None
+                         else torch.cuda.current_stream(logits.device).cuda_stream)
+    args = (_np_ptr(p), T, _dev_ptr(logits), vocab, _logits_dtype(logits), _dev_ptr(draft),
+            _dev_ptr(recent) if recent.numel() else None, recent.numel(), int(window), float(theta), st)
+    return args, (p, logits, draft, recent)
+
+
+def context_penalty(parent, logits, draft, recent, window, theta):
+    """Contextual penalty on every node's logits, in place (before accept_greedy)."""
+    args, _ = _penalty_args(parent, logits, draft, recent, window, theta, None)
+    _check(lib().tsw_context_penalty(*args), "tsw_context_penalty")
+    return logits
+
+
+def prepare_penalty(parent, logits, draft, recent, window, theta, stream=None):
+    args, keep = _penalty_args(parent, logits, draft, recent, window, theta, stream)
+    return PreparedCall(lib().tsw_context_penalty, args, "tsw_context_penalty", keep)
 
 
 def accept_greedy(parent, logits, draft, result=None, workspace=None):

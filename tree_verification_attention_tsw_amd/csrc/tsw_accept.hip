@@ -12,7 +12,10 @@
 // 文本生成", 技术原理, parallel-verification figure text (the longest valid
 // candidate is selected after checking against the full KV cache).
 //
-// Three kernels:
+// Kernels:
+//   context_penalty one work-group per node: the repetition penalty on the
+//                   logits of the tokens in the node's window (in place),
+//                   before the argmax when the caller asks for it.
 //   argmax_partial  grid (chunks, T): each work-group scans one slice of one
 //                   node's logits with 16-byte loads and keeps the largest
 //                   value (first index among equals).  HBM-bound.
@@ -178,7 +181,65 @@ __global__ __launch_bounds__(256) void kv_compact(const CompactArgs a, const int
     }
 }
 
+__device__ __forceinline__ void narrow_store(float* p, float x) { *p = x; }
+__device__ __forceinline__ void narrow_store(__bf16* p, float x) { *p = (__bf16)x; }   // nearest even
+
+// One work-group per tree node t.  Its window is the last `window` tokens of
+// the committed tokens (ending with the root's) followed by the draft tokens
+// on the path from the root down to t, i.e. what sequential generation had
+// produced before predicting the token after t.  Every logit the window names
+// is read and its penalised value formed before the work-group barrier, and
+// only then written, so a token that occurs several times is penalised once
+// (its writes all carry the same value).  Ids outside [0, vocab) are skipped.
+template <typename TIN>
+__global__ __launch_bounds__(256) void context_penalty(const PenaltyArgs a, TIN* __restrict__ logits,
+                                                       const int32_t* __restrict__ draft,
+                                                       const int32_t* __restrict__ recent) {
+    constexpr int PER = kPenaltyMaxWindow / 256;
+    __shared__ int32_t path[64];                     // path[0] = draft[t], then up towards the root
+    __shared__ int depth_s;
+    const int t = blockIdx.x;
+    if (threadIdx.x == 0) {
+        int d = 0;
+        for (int x = t; x != 0; x = a.parent[x]) path[d++] = draft[x];   // parent[x] < x: ends at the root
+        depth_s = d;
+    }
+    __syncthreads();
+    const int d = depth_s;
+    const int64_t total = a.n_recent + d;            // committed tokens, then the path (root side first)
+    const int64_t w = a.window < total ? a.window : total;
+    const int64_t first = total - w;
+    TIN* row = logits + (int64_t)t * a.vocab;
+    int32_t tok[PER];
+    float val[PER];
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+        const int64_t i = first + threadIdx.x + 256 * j;
+        int32_t v = -1;
+        if (i < total) v = i < a.n_recent ? recent[i] : path[d - 1 - (int)(i - a.n_recent)];
+        tok[j] = v >= 0 && v < a.vocab ? v : -1;
+        val[j] = tok[j] >= 0 ? widen(row[tok[j]]) : 0.0f;
+    }
+#pragma unroll
+    for (int j = 0; j < PER; ++j)
+        val[j] = val[j] > 0.0f ? __fdiv_rn(val[j], a.theta) : __fmul_rn(val[j], a.theta);
+    __syncthreads();                                 // every read done before any write
+#pragma unroll
+    for (int j = 0; j < PER; ++j)
+        if (tok[j] >= 0) narrow_store(row + tok[j], val[j]);
+}
+
 }  // namespace
+
+hipError_t launch_context_penalty(const PenaltyArgs& a, void* logits, int logits_dtype, const int32_t* draft,
+                                  const int32_t* recent, hipStream_t stream) {
+    if (logits_dtype == 0)
+        hipLaunchKernelGGL(context_penalty<float>, dim3(a.T), dim3(256), 0, stream, a, (float*)logits, draft, recent);
+    else
+        hipLaunchKernelGGL(context_penalty<__bf16>, dim3(a.T), dim3(256), 0, stream, a, (__bf16*)logits, draft,
+                           recent);
+    return hipGetLastError();
+}
 
 hipError_t launch_accept(const AcceptArgs& a, const void* logits, int logits_dtype, int64_t vocab, int64_t chunk,
                          bool vec_ok, const int32_t* draft, int32_t* result, AcceptPartial* part,

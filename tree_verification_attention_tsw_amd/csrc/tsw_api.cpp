@@ -464,6 +464,31 @@ int tsw_accept_greedy(const int32_t* parent, int32_t T, const void* logits, int6
                                          draft, result, (tsw::AcceptPartial*)workspace, (hipStream_t)stream));
 }
 
+int tsw_context_penalty(const int32_t* parent, int32_t T, void* logits, int64_t vocab, int32_t logits_dtype,
+                        const int32_t* draft, const int32_t* recent, int64_t n_recent, int32_t window, float theta,
+                        tsw_stream_t stream) {
+    int rc = check_accept_shape(T, vocab);
+    if (rc != TSW_OK) return rc;
+    tsw::PenaltyArgs a;
+    memset(&a, 0, sizeof a);
+    uint64_t mask[kMaxNodes];
+    rc = build_mask(parent, T, mask, nullptr);
+    if (rc != TSW_OK) return rc;
+    if (logits_dtype != TSW_DTYPE_F32 && logits_dtype != TSW_DTYPE_BF16) return TSW_EUNSUPPORTED;
+    if (window < 0 || window > tsw::kPenaltyMaxWindow || n_recent < 0) return TSW_EINVAL;
+    if (!(theta >= 1.0f) || !isfinite(theta)) return TSW_EINVAL;
+    if (!logits || (T > 1 && !draft) || (n_recent > 0 && !recent)) return TSW_EINVAL;
+    if (window == 0 || theta == 1.0f) return TSW_OK;     // nothing changes
+    a.T = T;
+    a.window = window;
+    a.vocab = vocab;
+    a.n_recent = n_recent;
+    a.theta = theta;
+    for (int i = 0; i < T; ++i) a.parent[i] = parent[i];
+    return hip_status(tsw::launch_context_penalty(a, logits, logits_dtype == TSW_DTYPE_F32 ? 0 : 1, draft, recent,
+                                                  (hipStream_t)stream));
+}
+
 int tsw_kv_compact(void* k, void* v, int32_t n_layers, int64_t layer_stride, int32_t Hkv, int32_t d, int32_t dtype,
                    int64_t kv_head_stride, int64_t n_prefix, int32_t T, const int32_t* result,
                    tsw_stream_t stream) {

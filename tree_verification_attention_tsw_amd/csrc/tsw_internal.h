@@ -112,6 +112,17 @@ hipError_t launch_accept(const AcceptArgs& a, const void* logits, int logits_dty
 hipError_t launch_kv_compact(const CompactArgs& a, int n_layers, int n_kv_heads, const int32_t* result,
                              hipStream_t stream);
 
+// Contextual penalty on every node's logits (in place).
+constexpr int kPenaltyMaxWindow = 8192;
+struct PenaltyArgs {
+    int32_t T, window;
+    int64_t vocab, n_recent;
+    float theta;
+    int32_t parent[64];
+};
+hipError_t launch_context_penalty(const PenaltyArgs& a, void* logits, int logits_dtype, const int32_t* draft,
+                                  const int32_t* recent, hipStream_t stream);
+
 // Importance of committed positions (node 0's attention mass) and the
 // draft pass's index selection.
 constexpr int kSelectChunk = 256;      // keys per importance work-group

@@ -143,6 +143,9 @@ class AcceptWorkload:
     n_prefix: int
     seed: int
     p_match: float = 0.8
+    penalty_window: int = 0      # contextual penalty before the argmax when > 0
+    theta: float = 1.0
+    n_recent: int = 4096         # committed tokens handed to the penalty
 
     def parent(self) -> np.ndarray:
         return kary_tree_parent(self.n_nodes, 3)
@@ -156,6 +159,11 @@ ACCEPT_WORKLOADS = {
     "accept_llama8b": AcceptWorkload("accept_llama8b", n_nodes=full_kary_nodes(3), vocab=128256,
                                      logits_dtype=F32, layers=32, Hkv=8, d=128, n_prefix=102400,
                                      seed=7000),
+    # the same step with the contextual penalty first (window and factor
+    # assumed: the pages give neither)
+    "accept_penalty_llama8b": AcceptWorkload("accept_penalty_llama8b", n_nodes=full_kary_nodes(3), vocab=128256,
+                                             logits_dtype=F32, layers=32, Hkv=8, d=128, n_prefix=102400,
+                                             seed=7000, penalty_window=1024, theta=1.2),
 }
 
 
