@@ -297,6 +297,16 @@ int tsw_context_penalty(const int32_t* parent, int32_t T, void* logits, int64_t 
                         const int32_t* draft, const int32_t* recent, int64_t n_recent, int32_t window, float theta,
                         tsw_stream_t stream);
 
+/* tsw_accept_greedy on the logits as tsw_context_penalty would leave them,
+ * without modifying them: each argmax work-group applies the penalty to the
+ * window tokens in its own slice of the vocabulary as it scans, so the step
+ * costs about one plain acceptance.  Arguments as for the two calls; the
+ * workspace is tsw_accept_workspace_size() bytes.  Errors as for both. */
+int tsw_accept_greedy_penalized(const int32_t* parent, int32_t T, const void* logits, int64_t vocab,
+                                int32_t logits_dtype, const int32_t* draft, const int32_t* recent, int64_t n_recent,
+                                int32_t window, float theta, int32_t* result, void* workspace,
+                                size_t workspace_bytes, tsw_stream_t stream);
+
 /* Moves the accepted path's K and V rows into place for n_layers caches:
  * for k = 1 .. L-1 the row at n_prefix + path[k] is copied to n_prefix + k
  * (row n_prefix + 0, the root, stays); the caller then commits

@@ -303,3 +303,18 @@ def test_penalty_argument_errors(L):
     assert call(parent=bad.ctypes.data_as(ctypes.c_void_p)) == EBADTREE
     assert call(window=0) == TSW_OK                       # nothing to do: no launch, no device needed
     assert call(theta=1.0) == TSW_OK
+
+
+def test_accept_penalized_argument_errors(L):
+    p = PARENT.ctypes.data_as(ctypes.c_void_p)
+
+    def call(window=64, theta=1.2, recent=FAKE, n_recent=10, ws=FAKE):
+        return L.tsw_accept_greedy_penalized(p, 13, FAKE, 1000, 0, FAKE, recent, n_recent, window, theta, FAKE, ws,
+                                             1 << 20, None)
+    assert call(window=-1) == EINVAL
+    assert call(window=8193) == EINVAL
+    assert call(theta=0.9) == EINVAL
+    assert call(theta=float("nan")) == EINVAL
+    assert call(recent=None) == EINVAL
+    assert call(n_recent=-2) == EINVAL
+    assert call(ws=None) == EINVAL

@@ -113,3 +113,44 @@ def test_penalty_then_accept_matches_oracle():
     say("penalty+accept: path %s bonus %d" % (path, bonus))
     assert res[0] == len(path) and res[1] == bonus and list(res[2:2 + len(path)]) == list(path)
     assert list(res[2 + T:2 + 2 * T]) == list(target)
+
+
+@pytest.mark.parametrize("T,vocab,n_recent,window,theta,dtype", [
+    (40, 128256, 5000, 1024, 1.2, "f32"),
+    (40, 128256, 5000, 1024, 1.2, "bf16"),
+    (40, 151936, 300, 8192, 1.7, "f32"),
+    (13, 5001, 64, 40, 3.0, "f32"),           # unaligned rows: the scalar scan
+    (13, 5001, 64, 40, 3.0, "bf16"),
+    (64, 2000, 10000, 700, 1.05, "bf16"),     # dense repeats, small vocabulary
+    (1, 128256, 2048, 2048, 1.3, "f32"),
+])
+def test_penalized_acceptance_matches_oracle(T, vocab, n_recent, window, theta, dtype):
+    """Acceptance with the penalty folded into the argmax: the oracle's
+    acceptance on the oracle's penalised logits, the logits left unchanged,
+    and the same result as the in-place penalty followed by acceptance."""
+    rng = np.random.default_rng(T * 7 + vocab + window)
+    parent = wl.kary_tree_parent(T, 3)
+    logits = rng.standard_normal((T, vocab)).astype(np.float32) * 3
+    best = logits.argmax(axis=1)
+    draft = np.array([best[parent[i]] if i else 0 for i in range(T)])
+    recent = np.concatenate([rng.integers(0, vocab, n_recent - 8), best[:8] if T >= 8 else rng.integers(0, vocab, 8)])
+    recent[::97] = -5                                  # ignored ids
+    lt = torch.from_numpy(logits).cuda()
+    if dtype == "bf16":
+        lt = lt.to(torch.bfloat16)
+        ref_in = lt.view(torch.int16).cpu().numpy().view(np.uint16)
+    else:
+        ref_in = logits
+    before = lt.clone()
+    res = tsw.accept_greedy_penalized(parent, lt, i32(draft), i32(recent), window, theta).cpu().numpy()
+    torch.cuda.synchronize()
+    assert torch.equal(lt.view(torch.int16) if dtype == "bf16" else lt,
+                       before.view(torch.int16) if dtype == "bf16" else before)
+    want_logits = pen.penalize(ref_in, parent, draft, recent, window, theta)
+    path, bonus, target = acc.accept_greedy(parent, want_logits, draft)
+    say("penalized accept T=%d vocab=%d window=%d %s: path %s bonus %d" % (T, vocab, window, dtype, path, bonus))
+    assert res[0] == len(path) and res[1] == bonus and list(res[2:2 + len(path)]) == list(path)
+    assert list(res[2 + T:2 + 2 * T]) == list(target)
+    tsw.context_penalty(parent, lt, i32(draft), i32(recent), window, theta)
+    res2 = tsw.accept_greedy(parent, lt, i32(draft)).cpu().numpy()
+    assert np.array_equal(res, res2)

@@ -14,7 +14,7 @@ from ._binding import (  # noqa: F401
     make_desc, plan_splits, status_str, tree_attn_partial, tree_attn_split, tree_attn_verify,
     tree_mask, workspace_size, PreparedCall, prepare_merge, prepare_split, prepare_verify,
     accept_workspace_size, accept_greedy, prepare_accept, kv_compact, prepare_compact,
-    context_penalty, prepare_penalty,
+    context_penalty, prepare_penalty, accept_greedy_penalized, prepare_accept_penalized,
     PagedDesc, make_paged_desc, paged_workspace_size, tree_attn_verify_paged, prepare_verify_paged,
     select_workspace_size, select_partial, prepare_select,
     verify_select_workspace_size, tree_attn_verify_select, prepare_verify_select,

@@ -73,6 +73,8 @@ def lib():
     L.tsw_verify_select_workspace_size.argtypes = [D, ctypes.POINTER(sz)]
     L.tsw_tree_attn_verify_select.argtypes = [D, vp, vp, vp, vp, vp, vp, i64, i64, vp, vp, vp, sz, vp]
     L.tsw_context_penalty.argtypes = [vp, i32, vp, i64, i32, vp, vp, i64, i32, ctypes.c_float, vp]
+    L.tsw_accept_greedy_penalized.argtypes = [vp, i32, vp, i64, i32, vp, vp, i64, i32, ctypes.c_float, vp, vp, sz,
+                                              vp]
     L.tsw_accept_workspace_size.argtypes = [i32, i64, ctypes.POINTER(sz)]
     L.tsw_accept_greedy.argtypes = [vp, i32, vp, i64, i32, vp, vp, vp, sz, vp]
     L.tsw_kv_compact.argtypes = [vp, vp, i32, i64, i32, i32, i32, i64, i64, i32, vp, vp]
@@ -395,6 +397,28 @@ def accept_greedy(parent, logits, draft, result=None, workspace=None):
     args, keep = _accept_args(parent, logits, draft, result, workspace, None)
     _check(lib().tsw_accept_greedy(*args), "tsw_accept_greedy")
     return keep[1]
+
+
+def _accept_penalized_args(parent, logits, draft, recent, window, theta, result, workspace, stream):
+    args, keep = _accept_args(parent, logits, draft, result, workspace, stream)
+    if recent.dtype != torch.int32 or not recent.is_cuda or not recent.is_contiguous():
+        raise ValueError("recent must be a contiguous int32 GPU tensor")
+    # (parent, T, logits, vocab, dtype, draft, result, workspace, bytes, stream) -> insert the penalty
+    full = args[:6] + (_dev_ptr(recent) if recent.numel() else None, recent.numel(), int(window),
+                       float(theta)) + args[6:]
+    return full, keep + (recent,)
+
+
+def accept_greedy_penalized(parent, logits, draft, recent, window, theta, result=None, workspace=None):
+    """Greedy acceptance on the contextually penalised logits (logits unchanged)."""
+    args, keep = _accept_penalized_args(parent, logits, draft, recent, window, theta, result, workspace, None)
+    _check(lib().tsw_accept_greedy_penalized(*args), "tsw_accept_greedy_penalized")
+    return keep[1]
+
+
+def prepare_accept_penalized(parent, logits, draft, recent, window, theta, result, workspace, stream=None):
+    args, keep = _accept_penalized_args(parent, logits, draft, recent, window, theta, result, workspace, stream)
+    return PreparedCall(lib().tsw_accept_greedy_penalized, args, "tsw_accept_greedy_penalized", keep)
 
 
 def prepare_accept(parent, logits, draft, result, workspace, stream=None):

@@ -60,9 +60,60 @@ __device__ __forceinline__ Best wave_best(Best x) {
 __device__ __forceinline__ float widen(float x) { return x; }
 __device__ __forceinline__ float widen(__bf16 x) { return (float)x; }
 
-template <typename TIN>
-__global__ __launch_bounds__(256) void argmax_partial(const TIN* __restrict__ logits, int64_t vocab,
-                                                      int64_t chunk, int n_chunks, bool vec_ok,
+// Node t's penalty window, oldest first: the last `window` tokens of the
+// committed tokens (ending with the root's) followed by the draft tokens on
+// the path from the root down to t.  The path's nodes come from the parent
+// array in the kernel arguments (scalar reads, no memory round trip); the
+// path tokens and this thread's committed tokens are then loaded together,
+// so the window costs one memory round trip.  Thread j of the work-group
+// gets window entries first + j + 256 * k in tok[k] (-1 past the end).
+constexpr int kWinPer = kPenaltyMaxWindow / 256;
+
+struct WindowLds {
+    int32_t nodes[64];
+    int32_t tok[64];
+    int depth;
+};
+
+__device__ __forceinline__ void load_window(const int32_t* parent, int32_t window, int64_t n_recent,
+                                            const int32_t* __restrict__ recent, const int32_t* __restrict__ draft,
+                                            int t, WindowLds& w, int32_t (&tok)[kWinPer]) {
+    if (threadIdx.x == 0) {
+        int d = 0;
+        for (int x = t; x != 0; x = parent[x]) w.nodes[d++] = x;   // parent[x] < x: ends at the root
+        w.depth = d;
+    }
+    __syncthreads();
+    const int d = w.depth;
+    if ((int)threadIdx.x < d) w.tok[threadIdx.x] = draft[w.nodes[threadIdx.x]];   // deepest first
+    const int64_t total = n_recent + d;
+    const int64_t first = total - (window < total ? window : total);
+#pragma unroll
+    for (int k = 0; k < kWinPer; ++k) {
+        const int64_t i = first + threadIdx.x + 256 * k;
+        tok[k] = i < n_recent && i < total ? recent[i] : -1;
+    }
+    __syncthreads();                                 // the path tokens are in LDS
+#pragma unroll
+    for (int k = 0; k < kWinPer; ++k) {
+        const int64_t i = first + threadIdx.x + 256 * k;
+        if (i >= n_recent && i < total) tok[k] = w.tok[d - 1 - (int)(i - n_recent)];
+    }
+}
+
+__device__ __forceinline__ float round_as(float x, float) { return x; }
+__device__ __forceinline__ float round_as(float x, __bf16) { return (float)(__bf16)x; }   // nearest even
+
+// One slice of one node's logits: the largest value and its first index.
+// With PEN the node's contextual penalty is applied on the fly: the window
+// tokens that fall in the slice are marked in an LDS bitmap and skipped by
+// the scan, and enter instead with their penalised values (formed from the
+// logits as given, so a repeated token counts once).  The logits are not
+// modified.
+template <typename TIN, bool PEN>
+__global__ __launch_bounds__(256) void argmax_partial(const AcceptArgs a, const TIN* __restrict__ logits,
+                                                      int64_t vocab, int64_t chunk, bool vec_ok,
+                                                      const int32_t* __restrict__ draft,
                                                       AcceptPartial* __restrict__ part) {
     constexpr int VEC = 16 / sizeof(TIN);
     const int t = blockIdx.y;
@@ -71,6 +122,44 @@ __global__ __launch_bounds__(256) void argmax_partial(const TIN* __restrict__ lo
     const int64_t start = (int64_t)c * chunk;
     const int64_t end = start + chunk < vocab ? start + chunk : vocab;
     Best b{-INFINITY, INT_MAX};
+    __shared__ uint32_t marks[PEN ? kAcceptSliceMax / 32 : 1];
+    __shared__ WindowLds wl;
+    if constexpr (PEN) {
+        const int nw = (int)((end - start + 31) >> 5);
+        for (int i = threadIdx.x; i < nw; i += 256) marks[i] = 0u;
+        int32_t tok[kWinPer];
+        load_window(a.parent, a.window, a.n_recent, a.recent, draft, t, wl, tok);   // barriers inside
+#pragma unroll
+        for (int k = 0; k < kWinPer; ++k) {
+            const int32_t v = tok[k];
+            if (v >= start && v < end) {
+                const uint32_t off = (uint32_t)(v - start);
+                atomicOr(&marks[off >> 5], 1u << (off & 31));
+                const float l = widen(row[v]);
+                const float p = round_as(l > 0.0f ? __fdiv_rn(l, a.theta) : __fmul_rn(l, a.theta), TIN{});
+                b = better(b, Best{p, v});
+            }
+        }
+        __syncthreads();
+    }
+    auto marked = [&](int64_t i) {
+        if constexpr (PEN) {
+            const uint32_t off = (uint32_t)(i - start);
+            return ((marks[off >> 5] >> (off & 31)) & 1u) != 0u;
+        } else {
+            return false;
+        }
+    };
+    // the marks of one vector's VEC elements (start is a multiple of 2048 and
+    // vectors are VEC-aligned within the slice, so they share one word)
+    auto field = [&](int64_t i) -> uint32_t {
+        if constexpr (PEN) {
+            const uint32_t off = (uint32_t)(i - start);
+            return (marks[off >> 5] >> (off & 31)) & ((1u << VEC) - 1u);
+        } else {
+            return 0u;
+        }
+    };
     if (vec_ok) {
         // start and the row are 16-byte aligned: whole vectors (four loads in
         // flight per lane), then the tail
@@ -83,18 +172,25 @@ __global__ __launch_bounds__(256) void argmax_partial(const TIN* __restrict__ lo
 #pragma unroll
             for (int u = 0; u < 4; ++u) x[u] = *(const vec_t*)(row + i + u * STEP);
 #pragma unroll
-            for (int u = 0; u < 4; ++u)
+            for (int u = 0; u < 4; ++u) {
+                const uint32_t f = field(i + u * STEP);
 #pragma unroll
-                for (int e = 0; e < VEC; ++e) b = better(b, Best{widen(x[u][e]), (int)(i + u * STEP + e)});
+                for (int e = 0; e < VEC; ++e)
+                    if (!((f >> e) & 1u)) b = better(b, Best{widen(x[u][e]), (int)(i + u * STEP + e)});
+            }
         }
         for (; i < vend; i += STEP) {
             const vec_t x = *(const vec_t*)(row + i);
+            const uint32_t f = field(i);
 #pragma unroll
-            for (int e = 0; e < VEC; ++e) b = better(b, Best{widen(x[e]), (int)(i + e)});
+            for (int e = 0; e < VEC; ++e)
+                if (!((f >> e) & 1u)) b = better(b, Best{widen(x[e]), (int)(i + e)});
         }
-        for (int64_t j = vend + threadIdx.x; j < end; j += 256) b = better(b, Best{widen(row[j]), (int)j});
+        for (int64_t j = vend + threadIdx.x; j < end; j += 256)
+            if (!marked(j)) b = better(b, Best{widen(row[j]), (int)j});
     } else {
-        for (int64_t i = start + threadIdx.x; i < end; i += 256) b = better(b, Best{widen(row[i]), (int)i});
+        for (int64_t i = start + threadIdx.x; i < end; i += 256)
+            if (!marked(i)) b = better(b, Best{widen(row[i]), (int)i});
     }
     b = wave_best(b);
     __shared__ Best wb[4];
@@ -102,7 +198,7 @@ __global__ __launch_bounds__(256) void argmax_partial(const TIN* __restrict__ lo
     __syncthreads();
     if (threadIdx.x == 0) {
         Best r = better(better(wb[0], wb[1]), better(wb[2], wb[3]));
-        part[(int64_t)t * n_chunks + c] = AcceptPartial{r.v, r.i};
+        part[(int64_t)t * a.n_chunks + c] = AcceptPartial{r.v, r.i};
     }
 }
 
@@ -195,38 +291,24 @@ template <typename TIN>
 __global__ __launch_bounds__(256) void context_penalty(const PenaltyArgs a, TIN* __restrict__ logits,
                                                        const int32_t* __restrict__ draft,
                                                        const int32_t* __restrict__ recent) {
-    constexpr int PER = kPenaltyMaxWindow / 256;
-    __shared__ int32_t path[64];                     // path[0] = draft[t], then up towards the root
-    __shared__ int depth_s;
+    __shared__ WindowLds wl;
     const int t = blockIdx.x;
-    if (threadIdx.x == 0) {
-        int d = 0;
-        for (int x = t; x != 0; x = a.parent[x]) path[d++] = draft[x];   // parent[x] < x: ends at the root
-        depth_s = d;
-    }
-    __syncthreads();
-    const int d = depth_s;
-    const int64_t total = a.n_recent + d;            // committed tokens, then the path (root side first)
-    const int64_t w = a.window < total ? a.window : total;
-    const int64_t first = total - w;
     TIN* row = logits + (int64_t)t * a.vocab;
-    int32_t tok[PER];
-    float val[PER];
+    int32_t tok[kWinPer];
+    load_window(a.parent, a.window, a.n_recent, recent, draft, t, wl, tok);
+    float val[kWinPer];
 #pragma unroll
-    for (int j = 0; j < PER; ++j) {
-        const int64_t i = first + threadIdx.x + 256 * j;
-        int32_t v = -1;
-        if (i < total) v = i < a.n_recent ? recent[i] : path[d - 1 - (int)(i - a.n_recent)];
-        tok[j] = v >= 0 && v < a.vocab ? v : -1;
-        val[j] = tok[j] >= 0 ? widen(row[tok[j]]) : 0.0f;
+    for (int k = 0; k < kWinPer; ++k) {
+        if (tok[k] >= a.vocab) tok[k] = -1;
+        val[k] = tok[k] >= 0 ? widen(row[tok[k]]) : 0.0f;
     }
 #pragma unroll
-    for (int j = 0; j < PER; ++j)
-        val[j] = val[j] > 0.0f ? __fdiv_rn(val[j], a.theta) : __fmul_rn(val[j], a.theta);
+    for (int k = 0; k < kWinPer; ++k)
+        val[k] = val[k] > 0.0f ? __fdiv_rn(val[k], a.theta) : __fmul_rn(val[k], a.theta);
     __syncthreads();                                 // every read done before any write
 #pragma unroll
-    for (int j = 0; j < PER; ++j)
-        if (tok[j] >= 0) narrow_store(row + tok[j], val[j]);
+    for (int k = 0; k < kWinPer; ++k)
+        if (tok[k] >= 0) narrow_store(row + tok[k], val[k]);
 }
 
 }  // namespace
@@ -245,12 +327,18 @@ hipError_t launch_accept(const AcceptArgs& a, const void* logits, int logits_dty
                          bool vec_ok, const int32_t* draft, int32_t* result, AcceptPartial* part,
                          hipStream_t stream) {
     const dim3 grid(a.n_chunks, a.T);
-    if (logits_dtype == 0)
-        hipLaunchKernelGGL(argmax_partial<float>, grid, dim3(256), 0, stream, (const float*)logits, vocab, chunk,
-                           a.n_chunks, vec_ok, part);
-    else
-        hipLaunchKernelGGL(argmax_partial<__bf16>, grid, dim3(256), 0, stream, (const __bf16*)logits, vocab, chunk,
-                           a.n_chunks, vec_ok, part);
+    const bool pen = a.window > 0;
+#define TSW_ARGMAX(TIN_, PEN_)                                                                                \
+    hipLaunchKernelGGL((argmax_partial<TIN_, PEN_>), grid, dim3(256), 0, stream, a, (const TIN_*)logits, vocab, \
+                       chunk, vec_ok, draft, part)
+    if (logits_dtype == 0) {
+        if (pen) TSW_ARGMAX(float, true);
+        else TSW_ARGMAX(float, false);
+    } else {
+        if (pen) TSW_ARGMAX(__bf16, true);
+        else TSW_ARGMAX(__bf16, false);
+    }
+#undef TSW_ARGMAX
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(accept_walk, dim3(1), dim3(64), 0, stream, a, part, draft, result);

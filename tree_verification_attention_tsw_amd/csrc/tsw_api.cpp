@@ -236,6 +236,7 @@ int accept_plan(int32_t T, int64_t vocab, int64_t* chunk, int32_t* n_chunks) {
     if (rc != TSW_OK) return rc;
     const int64_t per_node = cdiv(4 * (int64_t)cus, T);
     *chunk = cdiv(cdiv(vocab, per_node), kAcceptSliceQuantum) * kAcceptSliceQuantum;
+    if (*chunk > tsw::kAcceptSliceMax) *chunk = tsw::kAcceptSliceMax;
     *n_chunks = (int32_t)cdiv(vocab, *chunk);
     return TSW_OK;
 }
@@ -440,9 +441,11 @@ int tsw_accept_workspace_size(int32_t T, int64_t vocab, size_t* bytes) {
     return TSW_OK;
 }
 
-int tsw_accept_greedy(const int32_t* parent, int32_t T, const void* logits, int64_t vocab, int32_t logits_dtype,
-                      const int32_t* draft, int32_t* result, void* workspace, size_t workspace_bytes,
-                      tsw_stream_t stream) {
+namespace {
+
+int accept_call(const int32_t* parent, int32_t T, const void* logits, int64_t vocab, int32_t logits_dtype,
+                const int32_t* draft, const int32_t* recent, int64_t n_recent, int32_t window, float theta,
+                int32_t* result, void* workspace, size_t workspace_bytes, tsw_stream_t stream) {
     int rc = check_accept_shape(T, vocab);
     if (rc != TSW_OK) return rc;
     tsw::AcceptArgs a;
@@ -458,10 +461,35 @@ int tsw_accept_greedy(const int32_t* parent, int32_t T, const void* logits, int6
     if (workspace_bytes < (size_t)T * a.n_chunks * sizeof(tsw::AcceptPartial)) return TSW_ENOSPACE;
     a.T = T;
     for (int i = 0; i < T; ++i) a.parent[i] = parent[i];
+    a.window = window;
+    a.theta = theta;
+    a.n_recent = n_recent;
+    a.recent = recent;
     const int64_t esz = logits_dtype == TSW_DTYPE_F32 ? 4 : 2;
     const bool vec_ok = ((uintptr_t)logits & 15) == 0 && (vocab * esz) % 16 == 0;
     return hip_status(tsw::launch_accept(a, logits, logits_dtype == TSW_DTYPE_F32 ? 0 : 1, vocab, chunk, vec_ok,
                                          draft, result, (tsw::AcceptPartial*)workspace, (hipStream_t)stream));
+}
+
+}  // namespace
+
+int tsw_accept_greedy(const int32_t* parent, int32_t T, const void* logits, int64_t vocab, int32_t logits_dtype,
+                      const int32_t* draft, int32_t* result, void* workspace, size_t workspace_bytes,
+                      tsw_stream_t stream) {
+    return accept_call(parent, T, logits, vocab, logits_dtype, draft, nullptr, 0, 0, 1.0f, result, workspace,
+                       workspace_bytes, stream);
+}
+
+int tsw_accept_greedy_penalized(const int32_t* parent, int32_t T, const void* logits, int64_t vocab,
+                                int32_t logits_dtype, const int32_t* draft, const int32_t* recent, int64_t n_recent,
+                                int32_t window, float theta, int32_t* result, void* workspace,
+                                size_t workspace_bytes, tsw_stream_t stream) {
+    if (window < 0 || window > tsw::kPenaltyMaxWindow || n_recent < 0) return TSW_EINVAL;
+    if (!(theta >= 1.0f) || !isfinite(theta)) return TSW_EINVAL;
+    if (n_recent > 0 && !recent) return TSW_EINVAL;
+    if (theta == 1.0f) window = 0;                    // no penalty: the plain argmax
+    return accept_call(parent, T, logits, vocab, logits_dtype, draft, recent, n_recent, window, theta, result,
+                       workspace, workspace_bytes, stream);
 }
 
 int tsw_context_penalty(const int32_t* parent, int32_t T, void* logits, int64_t vocab, int32_t logits_dtype,

@@ -96,7 +96,14 @@ struct AcceptArgs {
     int32_t parent[64];
     int32_t depth[64];
     uint64_t mask[64];       // ancestor-or-self bits per node
+    // contextual penalty folded into the argmax (window > 0)
+    int32_t window;
+    float theta;
+    int64_t n_recent;
+    const int32_t* recent;
 };
+// Largest logit slice of one argmax work-group (its penalty bitmap in LDS).
+constexpr int64_t kAcceptSliceMax = 65536;
 // Accepted-path compaction of one cache (n_layers x Hkv heads of K and V).
 struct CompactArgs {
     void* k;
