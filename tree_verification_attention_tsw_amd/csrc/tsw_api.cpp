@@ -644,7 +644,10 @@ int tsw_select_partial(const tsw_attn_desc* desc, const void* q, const void* k, 
     a.d = desc->d;
     a.dtype = desc->dtype == TSW_DTYPE_F32 ? 0 : 1;
     a.scale = desc->scale;
-    rc = hip_status(tsw::launch_importance(a, imp, (hipStream_t)stream));
+    int cus = 0;
+    rc = device_cus(&cus);
+    if (rc != TSW_OK) return rc;
+    rc = hip_status(tsw::launch_importance(a, imp, cus, (hipStream_t)stream));
     if (rc != TSW_OK || n_out == 0) return rc;
     const int64_t keep = n_keep < n_out ? n_keep : n_out;
     return hip_status(tsw::launch_select(imp, desc->n_prefix, keep, n_out, idx, scratch, (hipStream_t)stream));
@@ -709,7 +712,10 @@ int tsw_tree_attn_verify_select(const tsw_attn_desc* desc, const void* q, const 
         a.d = desc->d;
         a.dtype = desc->dtype == TSW_DTYPE_F32 ? 0 : 1;
         a.scale = desc->scale;
-        rc = hip_status(tsw::launch_importance(a, imp, st));
+        int cus = 0;
+        rc = device_cus(&cus);
+        if (rc != TSW_OK) return rc;
+        rc = hip_status(tsw::launch_importance(a, imp, cus, st));
         if (rc != TSW_OK || n_out == 0) return rc;
         return hip_status(tsw::launch_select(imp, desc->n_prefix, keep, n_out, idx, scratch, st));
     }

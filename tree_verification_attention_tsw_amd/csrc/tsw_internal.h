@@ -142,7 +142,8 @@ struct SelectArgs {
     int32_t Hq, Hkv, G, d, dtype;
     float scale;
 };
-hipError_t launch_importance(const SelectArgs& a, float* imp, hipStream_t stream);
+// cus: the device's compute units (the key chunks are sized to two work-groups per CU)
+hipError_t launch_importance(const SelectArgs& a, float* imp, int cus, hipStream_t stream);
 constexpr int64_t kSelBlock = 4096;    // candidates per selection work-group
 size_t select_scratch_bytes(int64_t n_prefix);
 hipError_t launch_select(const float* imp, int64_t n_prefix, int64_t n_keep, int64_t n_out, int32_t* idx,

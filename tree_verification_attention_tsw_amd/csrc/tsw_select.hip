@@ -15,8 +15,9 @@
 // Kernels:
 //   importance_kernel  grid over key chunks: a work-group takes its chunk
 //                      through every kv head in turn (so the per-key sums are
-//                      formed in one fixed order, no atomics), a wavefront 16
-//                      keys at a time with lane (key, quarter of d).
+//                      formed in one fixed order, no atomics), a wavefront
+//                      holding 4 x 16 keys with lane (key, quarter of d), the
+//                      next head's rows loading while one head's are used.
 //   select_keep        the kept initial positions; clears the digit totals.
 //   importance_from_scores  the same importance from the root-row scores the
 //                      verification kernel wrote (K is not read again), with
@@ -44,52 +45,118 @@ __device__ __forceinline__ float widen_e(float x) { return x; }
 __device__ __forceinline__ float widen_e(__bf16 x) { return (float)x; }
 
 template <typename TIN, int D>
-__global__ __launch_bounds__(256) void importance_kernel(const SelectArgs a, float* __restrict__ imp) {
+__global__ __launch_bounds__(256) void importance_kernel(const SelectArgs a, int chunk, float* __restrict__ imp) {
     constexpr int QD = D / 4;                       // head-dim elements per lane
     constexpr int VEC = 16 / sizeof(TIN);           // elements per 16-byte load
+    constexpr int NV = QD / VEC;                    // loads per lane and key
+    constexpr int J = kSelectChunk / 64;            // 16-key groups per wave and head
+    // bf16 keys: the next kv head's rows are loaded while this one's are used
+    constexpr bool PF = sizeof(TIN) == 2;
     typedef TIN vec_t __attribute__((ext_vector_type(VEC)));
-    __shared__ float qs[kSelectMaxHeads * D];       // node 0's query heads
-    __shared__ float ls[kSelectMaxHeads];           // and their LSE
-    __shared__ float acc[kSelectChunk];             // per-key sums over heads
+    // node 0's query heads (as given: bf16 pairs or floats) and their LSE
+    __shared__ TIN qs[kSelectMaxHeads * D];
+    __shared__ float ls[kSelectMaxHeads];
 
-    const int64_t c0 = (int64_t)blockIdx.x * kSelectChunk;
-    const int n = (int)(a.n_prefix - c0 < kSelectChunk ? a.n_prefix - c0 : kSelectChunk);
+    // chunk <= kSelectChunk keys per work-group
+    const int64_t c0 = (int64_t)blockIdx.x * chunk;
+    const int n = (int)(a.n_prefix - c0 < chunk ? a.n_prefix - c0 : chunk);
     const TIN* q = (const TIN*)a.q;                 // row 0 = node 0
-    for (int i = threadIdx.x; i < a.Hq * D; i += 256) qs[i] = widen_e(q[i]);
+    for (int i = threadIdx.x; i < a.Hq * D; i += 256) qs[i] = q[i];
     for (int i = threadIdx.x; i < a.Hq; i += 256) ls[i] = a.lse[i];
-    for (int i = threadIdx.x; i < kSelectChunk; i += 256) acc[i] = 0.0f;
     __syncthreads();
 
+    // lane (li, lj) of wave w holds keys w*16 + j*64 + li (j < J), quarter lj
+    // of the head dim; every key's sum over the heads is formed by one lane
+    // in head order
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int li = lane & 15, lj = lane >> 4;
-    for (int g = 0; g < a.Hkv; ++g) {
+    float mine[J];
+#pragma unroll
+    for (int j = 0; j < J; ++j) mine[j] = 0.0f;
+    auto load = [&](int g, vec_t (&x)[J][NV]) {
         const TIN* kg = (const TIN*)a.k + (size_t)g * a.kv_head_stride;
-        for (int base = wave * 16; base < n; base += 64) {
-            const int key = base + li;
-            const bool ok = key < n;
-            const TIN* row = kg + (size_t)(c0 + (ok ? key : 0)) * D + lj * QD;
-            float kv[QD];
 #pragma unroll
-            for (int v = 0; v < QD / VEC; ++v) {
-                const vec_t x = *(const vec_t*)(row + v * VEC);
+        for (int j = 0; j < J; ++j) {
+            const int key = wave * 16 + j * 64 + li;
+            const TIN* row = kg + (size_t)(c0 + (key < n ? key : 0)) * D + lj * QD;
 #pragma unroll
-                for (int e = 0; e < VEC; ++e) kv[v * VEC + e] = widen_e(x[e]);
-            }
-            float sum = 0.0f;
-            for (int j = 0; j < a.G; ++j) {
-                const int h = g * a.G + j;
-                const float* qh = qs + h * D + lj * QD;
-                float dot = 0.0f;
-#pragma unroll
-                for (int e = 0; e < QD; ++e) dot = fmaf(qh[e], kv[e], dot);
-                dot = quad_sum(dot);
-                sum += __expf(dot * a.scale - ls[h]);
-            }
-            if (ok && lj == 0) acc[key] += sum;
+            for (int v = 0; v < NV; ++v) x[j][v] = *(const vec_t*)(row + v * VEC);
         }
-        __syncthreads();
+    };
+    // one kv head: each query head's quarter is read from LDS once and used
+    // for all J key groups; bf16 pairs go through v_dot2_f32_bf16 (products
+    // of bf16 values are exact in float32), floats through FMAs
+    auto use = [&](int g, const vec_t (&x)[J][NV]) {
+        float sum[J];
+#pragma unroll
+        for (int j = 0; j < J; ++j) sum[j] = 0.0f;
+        for (int jj = 0; jj < a.G; ++jj) {
+            const int h = g * a.G + jj;
+            const float lh = ls[h];
+            float dot[J];
+            if constexpr (sizeof(TIN) == 2) {
+                const bf16x2* qh = (const bf16x2*)(qs + h * D + lj * QD);
+                bf16x2 qv[QD / 2];
+#pragma unroll
+                for (int e = 0; e < QD / 2; ++e) qv[e] = qh[e];
+#pragma unroll
+                for (int j = 0; j < J; ++j) {
+                    float acc = 0.0f;
+#pragma unroll
+                    for (int v = 0; v < NV; ++v)
+#pragma unroll
+                        for (int e = 0; e < VEC; e += 2) {
+                            const bf16x2 kp = {x[j][v][e], x[j][v][e + 1]};
+                            acc = __builtin_amdgcn_fdot2_f32_bf16(kp, qv[(v * VEC + e) / 2], acc, false);
+                        }
+                    dot[j] = acc;
+                }
+            } else {
+                const float* qh = (const float*)(qs + h * D + lj * QD);
+                float qv[QD];
+#pragma unroll
+                for (int e = 0; e < QD; ++e) qv[e] = qh[e];
+#pragma unroll
+                for (int j = 0; j < J; ++j) {
+                    float acc = 0.0f;
+#pragma unroll
+                    for (int v = 0; v < NV; ++v)
+#pragma unroll
+                        for (int e = 0; e < VEC; ++e) acc = fmaf(qv[v * VEC + e], widen_e(x[j][v][e]), acc);
+                    dot[j] = acc;
+                }
+            }
+#pragma unroll
+            for (int j = 0; j < J; ++j) sum[j] += __expf(quad_sum(dot[j]) * a.scale - lh);
+        }
+#pragma unroll
+        for (int j = 0; j < J; ++j) mine[j] += sum[j];
+    };
+    if constexpr (PF) {
+        vec_t xa[J][NV], xb[J][NV];
+        load(0, xa);
+        int g = 0;
+        for (; g + 1 < a.Hkv; g += 2) {
+            load(g + 1, xb);
+            use(g, xa);
+            if (g + 2 < a.Hkv) load(g + 2, xa);
+            use(g + 1, xb);
+        }
+        if (g < a.Hkv) use(g, xa);
+    } else {
+        vec_t x[J][NV];
+        for (int g = 0; g < a.Hkv; ++g) {
+            load(g, x);
+            use(g, x);
+        }
     }
-    for (int i = threadIdx.x; i < n; i += 256) imp[c0 + i] = acc[i];
+    if (lj == 0) {
+#pragma unroll
+        for (int j = 0; j < J; ++j) {
+            const int key = wave * 16 + j * 64 + li;
+            if (key < n) imp[c0 + key] = mine[j];
+        }
+    }
 }
 
 // Selection state after `passes` radix passes, derived from the digit totals
@@ -366,15 +433,22 @@ __global__ __launch_bounds__(256) void select_write(const uint32_t* __restrict__
 
 }  // namespace
 
-hipError_t launch_importance(const SelectArgs& a, float* imp, hipStream_t stream) {
-    const dim3 grid((unsigned)((a.n_prefix + kSelectChunk - 1) / kSelectChunk));
+hipError_t launch_importance(const SelectArgs& a, float* imp, int cus, hipStream_t stream) {
     if (a.n_prefix == 0) return hipSuccess;
+    // two work-groups per CU when the keys allow (a whole round, evenly
+    // loaded), at most kSelectChunk keys each, a multiple of 16
+    const int64_t want = 2 * (int64_t)(cus > 0 ? cus : 1);
+    int64_t chunk = (a.n_prefix + want - 1) / want;
+    chunk = (chunk + 15) / 16 * 16;
+    if (chunk > kSelectChunk) chunk = kSelectChunk;
+    const dim3 grid((unsigned)((a.n_prefix + chunk - 1) / chunk));
+    const int c = (int)chunk;
     if (a.dtype == 0) {
-        if (a.d == 128) hipLaunchKernelGGL((importance_kernel<float, 128>), grid, dim3(256), 0, stream, a, imp);
-        else hipLaunchKernelGGL((importance_kernel<float, 64>), grid, dim3(256), 0, stream, a, imp);
+        if (a.d == 128) hipLaunchKernelGGL((importance_kernel<float, 128>), grid, dim3(256), 0, stream, a, c, imp);
+        else hipLaunchKernelGGL((importance_kernel<float, 64>), grid, dim3(256), 0, stream, a, c, imp);
     } else {
-        if (a.d == 128) hipLaunchKernelGGL((importance_kernel<__bf16, 128>), grid, dim3(256), 0, stream, a, imp);
-        else hipLaunchKernelGGL((importance_kernel<__bf16, 64>), grid, dim3(256), 0, stream, a, imp);
+        if (a.d == 128) hipLaunchKernelGGL((importance_kernel<__bf16, 128>), grid, dim3(256), 0, stream, a, c, imp);
+        else hipLaunchKernelGGL((importance_kernel<__bf16, 64>), grid, dim3(256), 0, stream, a, c, imp);
     }
     return hipGetLastError();
 }
