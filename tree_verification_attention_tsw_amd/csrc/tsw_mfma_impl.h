@@ -18,9 +18,10 @@
 // eight (two per SIMD, 256 registers), each owning NB or NB-1 blocks of 16
 // query rows (R row groups) and one 32-key sub-tile of every key tile
 // (W/R sub-tiles per tile).  Per tile:
-//   * K and V rows move HBM -> LDS with global_load_lds_dwordx4 into a
-//     128 KB ring (2, 4 or 8 stages); explicit s_waitcnt vmcnt keeps later
-//     tiles in flight, and one work-group barrier per tile recycles stages.
+//   * K and V rows move HBM -> LDS with global_load_lds_dwordx4 (streaming
+//     cache policy) into a 128 KB ring of two 128-key load groups: one group
+//     is in flight while the other is computed on, and one work-group
+//     barrier per group recycles its stages.
 //   * S^T = K Q^T on v_mfma_f32_16x16x32_bf16 with key rows on the M axis and
 //     query rows on N, so every lane owns one query row of each block.
 //   * O += P V on the same instruction (queries on rows); V operands come
@@ -66,17 +67,22 @@ struct Shape {
     static constexpr int MASK_BYTES = 64 * 8;
     static constexpr int IDX_BYTES = MODE_ != kModeContig ? kGatherChunkMax * 4 : 0;
     static constexpr int RESERVE = ((POOL + MASK_BYTES + 255) & ~255) + IDX_BYTES;
-    // as many stages as the LDS holds (up to 16): more tiles in flight
+    // Loads are issued, waited for and recycled in groups of GT tiles, 128
+    // keys (32 KB of K and 32 KB of V) per group, with one barrier per group.
+    // The ring holds two groups, one in flight while the other is computed
+    // on; on MI355X that streams faster than more, smaller stages in the
+    // same LDS.
+    static constexpr int GT = TK >= 128 ? 1 : 128 / TK;
     static constexpr int STAGES_FIT = (160 * 1024 - RESERVE) / STAGE;
-    static constexpr int STAGES = STAGES_FIT < 16 ? STAGES_FIT : 16;
+    static constexpr int STAGES = 2 * GT;
     static constexpr int RING = STAGES * STAGE;
     static constexpr int XSLOTS = (KS - 1) * R * NB;   // parked (wave, block) pairs
     static constexpr int XBYTES = XSLOTS * (8 * 64 * 16 + 32 * 4);
     // ring (+ index slice) during the loop, the KS exchange afterwards
     static constexpr int LOOP_BYTES = RING + IDX_BYTES;
     static constexpr int SMEM = LOOP_BYTES > XBYTES ? LOOP_BYTES : XBYTES;
-    static_assert(STAGES >= 2, "at least two ring stages");
-    static_assert((STAGES - 1) * NI < 64, "vmcnt range");
+    static_assert(STAGES <= STAGES_FIT, "two load groups fit the LDS");
+    static_assert(GT * NI < 64, "vmcnt range");
 };
 
 struct Ctx {
@@ -118,7 +124,8 @@ __device__ __forceinline__ void issue_tile(const SplitArgs& a, const Ctx& cx, in
             const uint32_t off = (uint32_t)(row * S::ROWB + 16 * (cx.li ^ swz(row)));
             char* dst = sbase + (isv ? S::TK * S::ROWB : 0) + grp * 1024;
             __builtin_amdgcn_global_load_lds((const void*)((isv ? vt : kt) + off),
-                                             (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
+                                             (__attribute__((address_space(3))) void*)dst, 16, 0,
+                                             kStreamAux);
         }
         return;
     }
@@ -142,7 +149,7 @@ __device__ __forceinline__ void issue_tile(const SplitArgs& a, const Ctx& cx, in
             const char* src = (isv ? cx.vbase : cx.kbase) + pos * S::ROWB + 16 * (cx.li ^ swz(row));
             char* dst = sbase + (isv ? S::TK * S::ROWB : 0) + grp * 1024;
             __builtin_amdgcn_global_load_lds((const void*)src, (__attribute__((address_space(3))) void*)dst, 16, 0,
-                                             0);
+                                             kStreamAux);
         }
     } else {
         // paged: every load's page number is read from the staged table
@@ -177,23 +184,8 @@ __device__ __forceinline__ void issue_tile(const SplitArgs& a, const Ctx& cx, in
                               (uint32_t)((pos[i] & (a.page_rows - 1)) * S::ROWB + 16 * (cx.li ^ swz(row)));
             char* dst = sbase + (isv ? S::TK * S::ROWB : 0) + grp * 1024;
             __builtin_amdgcn_global_load_lds((const void*)src, (__attribute__((address_space(3))) void*)dst, 16, 0,
-                                             0);
+                                             kStreamAux);
         }
-    }
-}
-
-// Wait until this wave's loads of the oldest pending tile have landed while
-// `newer` later tiles stay in flight (0 <= newer <= K).
-template <class S, int K = S::STAGES - 2>
-__device__ __forceinline__ void wait_tile(int newer) {
-    if constexpr (K <= 0) {
-        wait_vmcnt<0>();
-    } else {
-        if (newer >= K) {
-            wait_vmcnt<K * S::NI>();
-            return;
-        }
-        wait_tile<S, K - 1>(newer);
     }
 }
 
@@ -433,16 +425,17 @@ __device__ __forceinline__ void run_wave(const SplitArgs& a, const Ctx& cx) {
 #pragma unroll
         for (int s = 0; s < 4; ++s) qop[b][s] = src[4 * s];
     }
-    // The fast pass's first tiles go out right behind the Q loads; the wait
-    // below lets exactly those tile loads stay in flight, so the Q latency
-    // hides under the first tile's and the tile loop never waits on Q.
-    if (n >= STAGES - 1) {
+    // The fast pass's first load group goes out right behind the Q loads;
+    // the wait below lets exactly those tile loads stay in flight, so the Q
+    // latency hides under the first group's and the tile loop never waits
+    // on Q.
+    if (n >= S::GT) {
 #pragma unroll
-        for (int s = 0; s < STAGES - 1; ++s) issue_tile<S, LAYOUT>(a, cx, s, s);
-        wait_vmcnt<(STAGES - 1) * S::NI>();
+        for (int s = 0; s < S::GT; ++s) issue_tile<S, LAYOUT>(a, cx, s, s);
+        wait_vmcnt<S::GT * S::NI>();
     } else {
 #pragma unroll
-        for (int s = 0; s < STAGES - 1; ++s)
+        for (int s = 0; s < S::GT; ++s)
             if (s < n) issue_tile<S, LAYOUT>(a, cx, s, s);
         wait_vmcnt<0>();
     }
@@ -459,7 +452,8 @@ __device__ __forceinline__ void run_wave(const SplitArgs& a, const Ctx& cx) {
     bf16x8 kop[2][4], vop[8];
 
     // One pass over the split's tiles; every pass crosses one barrier per
-    // tile (plus one at the start of a rerun), identically in all waves.
+    // load group (plus one at the start of a rerun), identically in all
+    // waves.
     //   FAST: p = 2^(s*c);  MAXONLY: exact row maxima;  EXACT: p = 2^(s*c - m).
     // The fast pass's first tiles are already in flight.
     constexpr int FAST = 0, MAXONLY = 1, EXACT = 2;
@@ -470,7 +464,7 @@ __device__ __forceinline__ void run_wave(const SplitArgs& a, const Ctx& cx) {
             // previous pass's last tile
             barrier_lds();
 #pragma unroll
-            for (int s = 0; s < STAGES - 1; ++s)
+            for (int s = 0; s < S::GT; ++s)
                 if (s < n) issue_tile<S, LAYOUT>(a, cx, s, s);
         }
         // Full prefix tiles come first; the ragged end of the slice and the
@@ -479,12 +473,16 @@ __device__ __forceinline__ void run_wave(const SplitArgs& a, const Ctx& cx) {
         const int n_full = (int)((cx.c1 - cx.c0) / S::TK);
         auto step = [&](int t, auto masked_c) {
             constexpr bool MASKED = decltype(masked_c)::value;
-            // Tiles issued so far end at min(n-1, t+STAGES-2).
-            const int newer = n - 1 - t < STAGES - 2 ? n - 1 - t : STAGES - 2;
-            wait_tile<S>(newer);
-            barrier_lds();
-            // The stage of tile t-1 is free once every wave passed the barrier.
-            if (t + STAGES - 1 < n) issue_tile<S, LAYOUT>(a, cx, t + STAGES - 1, (t + STAGES - 1) % STAGES);
+            if (t % S::GT == 0) {
+                // The group starting at tile t is the only one in flight.
+                wait_vmcnt<0>();
+                barrier_lds();
+                // The previous group's stages are free once every wave passed
+                // the barrier; the next group goes into them.
+#pragma unroll
+                for (int j = 0; j < S::GT; ++j)
+                    if (t + S::GT + j < n) issue_tile<S, LAYOUT>(a, cx, t + S::GT + j, (t + S::GT + j) % STAGES);
+            }
             const char* Ks = cx.smem + (t % STAGES) * S::STAGE;
             if constexpr (MODE == MAXONLY) {
                 load_k<S>(Ks, cx, kop);
