@@ -73,6 +73,17 @@ __device__ __forceinline__ bf16x4 ds_read_tr16_b64(const char* p) {
     return r;
 }
 
+// The same read at p + OFF, the constant in the instruction's offset field
+// (no address arithmetic for it).
+template <int OFF>
+__device__ __forceinline__ bf16x4 ds_read_tr16_b64_at(const char* p) {
+    static_assert(OFF >= 0 && OFF < 65536, "LDS instruction offset range");
+    bf16x4 r;
+    const uint32_t a = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
+    asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(a), "i"(OFF));
+    return r;
+}
+
 // Wait for every outstanding LDS read (and scalar load); tying the values
 // keeps their uses after the wait.
 __device__ __forceinline__ void lds_wait(bf16x4& x, bf16x4& y) {

@@ -190,13 +190,15 @@ __device__ __forceinline__ void issue_tile(const SplitArgs& a, const Ctx& cx, in
 }
 
 // K operands of this wave's 32-key sub-tile: lane (li, lj) holds key row
-// kb*16 + li, head-dim elements 32*s + 8*lj .. +7.
-template <class S>
+// kb*16 + li, head-dim elements 32*s + 8*lj .. +7.  The tile's stage is Ks +
+// SOFF; a constant SOFF lands in the reads' offset fields, so the tiles of a
+// load group share their address arithmetic.
+template <class S, int SOFF = 0>
 __device__ __forceinline__ void load_k(const char* Ks, const Ctx& cx, bf16x8 (&kop)[2][4]) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
         const int row = cx.ks * 32 + kb * 16 + cx.li;
-        const char* base = Ks + row * S::ROWB;
+        const char* base = Ks + SOFF + row * S::ROWB;
         const int sw = swz(row);
 #pragma unroll
         for (int s = 0; s < 4; ++s) kop[kb][s] = *(const bf16x8*)(base + 16 * ((4 * s + cx.lj) ^ sw));
@@ -205,20 +207,21 @@ __device__ __forceinline__ void load_k(const char* Ks, const Ctx& cx, bf16x8 (&k
 
 // V operands: the transposed reads give lane (li, lj) V[key][16*db + li] for
 // keys 4*lj .. 4*lj+3 of each 16-key half, matching P's K-slot layout.
-template <class S>
-__device__ __forceinline__ void load_v(const char* Vs, const Ctx& cx, bf16x8 (&vop)[8]) {
+// Rows trow and trow + 16 share their swizzle (it depends on the low four
+// row bits only), so the second half is the first at a constant offset.
+// The V tile follows the K tile in the stage at Ks + SOFF.
+template <class S, int SOFF = 0>
+__device__ __forceinline__ void load_v(const char* Ks, const Ctx& cx, bf16x8 (&vop)[8]) {
+    constexpr int VOFF = SOFF + S::TK * S::ROWB;
     const int trow0 = cx.ks * 32 + 4 * cx.lj + (cx.li >> 2);
-    const int trow1 = trow0 + 16;
     const int tsel = (cx.li >> 1) & 1;
-    const char* vrow0 = Vs + trow0 * S::ROWB + 8 * (cx.li & 1);
-    const char* vrow1 = Vs + trow1 * S::ROWB + 8 * (cx.li & 1);
+    const char* vrow0 = Ks + trow0 * S::ROWB + 8 * (cx.li & 1);
     const int sw0 = swz(trow0) ^ tsel;
-    const int sw1 = swz(trow1) ^ tsel;
     bf16x4 v0[8], v1[8];
 #pragma unroll
     for (int db = 0; db < 8; ++db) {
-        v0[db] = ds_read_tr16_b64(vrow0 + 16 * ((2 * db) ^ sw0));
-        v1[db] = ds_read_tr16_b64(vrow1 + 16 * ((2 * db) ^ sw1));
+        v0[db] = ds_read_tr16_b64_at<VOFF>(vrow0 + 16 * ((2 * db) ^ sw0));
+        v1[db] = ds_read_tr16_b64_at<VOFF + 16 * S::ROWB>(vrow0 + 16 * ((2 * db) ^ sw0));
     }
 #pragma unroll
     for (int db = 0; db < 8; ++db) {
@@ -340,9 +343,9 @@ __device__ __forceinline__ void tile_pv(const SplitArgs& a, const Ctx& cx, int t
 // exponentials of all blocks, then P V one V column block at a time, so only
 // a step's K operands and one V operand are live.  The other wave on the
 // SIMD fills the matrix pipe while this one exponentiates.
-template <class S, int NBA, bool MASKED, bool SHIFT, bool EMIT>
+template <class S, int NBA, bool MASKED, bool SHIFT, bool EMIT, int SOFF = 0>
 __device__ __forceinline__ void tile_pv_shared(const SplitArgs& a, const Ctx& cx, int tt, float c, const char* Ks,
-                                               const char* Vs, const bf16x8 (&qop)[NBA][4], const float (&m)[NBA],
+                                               const bf16x8 (&qop)[NBA][4], const float (&m)[NBA],
                                                float (&l)[NBA], f32x4 (&o)[NBA][8]) {
     f32x4 sc[NBA][2];
 #pragma unroll
@@ -350,7 +353,7 @@ __device__ __forceinline__ void tile_pv_shared(const SplitArgs& a, const Ctx& cx
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
         const int row = cx.ks * 32 + kb * 16 + cx.li;
-        const char* base = Ks + row * S::ROWB;
+        const char* base = Ks + SOFF + row * S::ROWB;
         const int sw = swz(row);
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
@@ -365,24 +368,25 @@ __device__ __forceinline__ void tile_pv_shared(const SplitArgs& a, const Ctx& cx
 #pragma unroll
     for (int b = 0; b < NBA; ++b)
         softmax_block<SHIFT>(sc[b], c, (SHIFT && m[b] != -INFINITY) ? m[b] : 0.0f, l[b], pb[b]);
+    // V rows are addressed from the K stage: the stage offset, the V tile
+    // and the second 16-row half (same swizzle) are constant offsets of the
+    // read.
+    constexpr int VOFF = SOFF + S::TK * S::ROWB;
     const int trow0 = cx.ks * 32 + 4 * cx.lj + (cx.li >> 2);
-    const int trow1 = trow0 + 16;
     const int tsel = (cx.li >> 1) & 1;
-    const char* vrow0 = Vs + trow0 * S::ROWB + 8 * (cx.li & 1);
-    const char* vrow1 = Vs + trow1 * S::ROWB + 8 * (cx.li & 1);
+    const char* vrow0 = Ks + trow0 * S::ROWB + 8 * (cx.li & 1);
     const int sw0 = swz(trow0) ^ tsel;
-    const int sw1 = swz(trow1) ^ tsel;
     // V operands for column block db+1 are read while the products of block
     // db run.
-    bf16x4 c0 = ds_read_tr16_b64(vrow0 + 16 * (0 ^ sw0));
-    bf16x4 c1 = ds_read_tr16_b64(vrow1 + 16 * (0 ^ sw1));
+    bf16x4 c0 = ds_read_tr16_b64_at<VOFF>(vrow0 + 16 * (0 ^ sw0));
+    bf16x4 c1 = ds_read_tr16_b64_at<VOFF + 16 * S::ROWB>(vrow0 + 16 * (0 ^ sw0));
 #pragma unroll
     for (int db = 0; db < 8; ++db) {
         lds_wait(c0, c1);
         const bf16x8 vop = __builtin_shufflevector(c0, c1, 0, 1, 2, 3, 4, 5, 6, 7);
         if (db + 1 < 8) {
-            c0 = ds_read_tr16_b64(vrow0 + 16 * ((2 * (db + 1)) ^ sw0));
-            c1 = ds_read_tr16_b64(vrow1 + 16 * ((2 * (db + 1)) ^ sw1));
+            c0 = ds_read_tr16_b64_at<VOFF>(vrow0 + 16 * ((2 * (db + 1)) ^ sw0));
+            c1 = ds_read_tr16_b64_at<VOFF + 16 * S::ROWB>(vrow0 + 16 * ((2 * (db + 1)) ^ sw0));
         }
 #pragma unroll
         for (int b = 0; b < NBA; ++b) o[b][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pb[b], vop, o[b][db], 0, 0, 0);
@@ -468,39 +472,60 @@ __device__ __forceinline__ void run_wave(const SplitArgs& a, const Ctx& cx) {
                 if (s < n) issue_tile<S, LAYOUT>(a, cx, s, s);
         }
         // Full prefix tiles come first; the ragged end of the slice and the
-        // tree's own rows (masked) come last, so the two kinds run in two
-        // consecutive loops with one copy of the tile code each.
+        // tree's own rows (masked) come last, so the two kinds run in
+        // separate loops with one copy of the tile code each.
         const int n_full = (int)((cx.c1 - cx.c0) / S::TK);
-        auto step = [&](int t, auto masked_c) {
-            constexpr bool MASKED = decltype(masked_c)::value;
-            if (t % S::GT == 0) {
-                // The group starting at tile t is the only one in flight.
-                wait_vmcnt<0>();
-                barrier_lds();
-                // The previous group's stages are free once every wave passed
-                // the barrier; the next group goes into them.
+        auto group_start = [&](int t) {
+            // The group starting at tile t is the only one in flight.
+            wait_vmcnt<0>();
+            barrier_lds();
+            // The previous group's stages are free once every wave passed
+            // the barrier; the next group goes into them.
 #pragma unroll
-                for (int j = 0; j < S::GT; ++j)
-                    if (t + S::GT + j < n) issue_tile<S, LAYOUT>(a, cx, t + S::GT + j, (t + S::GT + j) % STAGES);
-            }
-            const char* Ks = cx.smem + (t % STAGES) * S::STAGE;
+            for (int j = 0; j < S::GT; ++j)
+                if (t + S::GT + j < n) issue_tile<S, LAYOUT>(a, cx, t + S::GT + j, (t + S::GT + j) % STAGES);
+        };
+        // One tile from stage Ks + SOFF.
+        auto tile = [&](int t, const char* Ks, auto masked_c, auto soff_c) {
+            constexpr bool MASKED = decltype(masked_c)::value;
+            constexpr int SOFF = decltype(soff_c)::value;
             if constexpr (MODE == MAXONLY) {
-                load_k<S>(Ks, cx, kop);
+                load_k<S, SOFF>(Ks, cx, kop);
                 tile_max<S, NBA, MASKED>(a, cx, t, c, kop, qop, m_run);
             } else if constexpr (S::WAVES == 8) {
-                tile_pv_shared<S, NBA, MASKED, MODE == EXACT, EMIT && MODE == FAST>(a, cx, t, c, Ks,
-                                                                                   Ks + S::TK * S::ROWB, qop,
-                                                                                   m_run, l_run, o);
+                tile_pv_shared<S, NBA, MASKED, MODE == EXACT, EMIT && MODE == FAST, SOFF>(a, cx, t, c, Ks, qop, m_run,
+                                                                                         l_run, o);
             } else {
-                load_k<S>(Ks, cx, kop);
-                load_v<S>(Ks + S::TK * S::ROWB, cx, vop);
+                load_k<S, SOFF>(Ks, cx, kop);
+                load_v<S, SOFF>(Ks, cx, vop);
                 tile_pv<S, NBA, MASKED, MODE == EXACT, EMIT && MODE == FAST>(a, cx, t, c, kop, vop, qop, m_run,
                                                                             l_run, o);
             }
         };
+        using Unmasked = std::false_type;
+        using Masked = std::true_type;
         int t = 0;
-        for (; t < n_full; ++t) step(t, std::false_type{});
-        for (; t < n; ++t) step(t, std::true_type{});
+        // Whole groups of full tiles: the group's tiles are unrolled so
+        // their stage offsets are constants.
+        for (; t + S::GT <= n_full; t += S::GT) {
+            group_start(t);
+            const char* gb = cx.smem + (t % STAGES) * S::STAGE;
+            tile(t, gb, Unmasked{}, std::integral_constant<int, 0>{});
+            if constexpr (S::GT >= 2) tile(t + 1, gb, Unmasked{}, std::integral_constant<int, S::STAGE>{});
+            if constexpr (S::GT >= 4) {
+                tile(t + 2, gb, Unmasked{}, std::integral_constant<int, 2 * S::STAGE>{});
+                tile(t + 3, gb, Unmasked{}, std::integral_constant<int, 3 * S::STAGE>{});
+            }
+        }
+        static_assert(S::GT == 1 || S::GT == 2 || S::GT == 4, "load group size");
+        for (; t < n_full; ++t) {
+            if (t % S::GT == 0) group_start(t);
+            tile(t, cx.smem + (t % STAGES) * S::STAGE, Unmasked{}, std::integral_constant<int, 0>{});
+        }
+        for (; t < n; ++t) {
+            if (t % S::GT == 0) group_start(t);
+            tile(t, cx.smem + (t % STAGES) * S::STAGE, Masked{}, std::integral_constant<int, 0>{});
+        }
     };
 
     pass(std::integral_constant<int, FAST>{});
