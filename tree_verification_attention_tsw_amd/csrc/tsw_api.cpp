@@ -99,18 +99,37 @@ int device_cus(int* cus) {
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// Tiles of the longest slice when n_keys prefix keys are cut into ns parts
+// of run_split's chunk size and the last part also takes the tree's tiles.
+int64_t longest_slice_tiles(int64_t n_keys, int64_t ns, int64_t tk, int64_t tree_tiles) {
+    const int64_t chunk = cdiv(cdiv(n_keys, ns), tk) * tk;
+    int64_t last = n_keys - (ns - 1) * chunk;
+    if (last < 0) last = 0;
+    const int64_t c = chunk / tk, l = cdiv(last, tk) + tree_tiles;
+    return c > l ? c : l;
+}
+
 // Split-K degree: enough work-groups to occupy every CU once (the matrix
 // kernel runs one work-group per CU), no split shorter than two key tiles,
-// and gather slices that fit the LDS index buffer.
+// and gather slices that fit the LDS index buffer.  When a CU is still free
+// per kv head and one more split shortens the longest slice (the last one
+// carries the tree's own tiles after its share of the prefix), take it: the
+// tree rows then get a split of their own or a shorter prefix share.
 int plan(const tsw_attn_desc* d, int64_t n_keys, bool gather, int cus, int32_t* n_splits) {
     tsw::MfmaConfig cfg;
     int64_t s;
     if (use_mfma(d, n_keys, &cfg)) {
         const int64_t tk = cfg.tile_keys();
-        s = cus / d->Hkv;
-        if (s < 1) s = 1;
+        int64_t smax = cus / d->Hkv;
+        if (smax < 1) smax = 1;
+        s = smax;
         const int64_t by_len = cdiv(n_keys, 2 * tk);
         if (s > by_len) s = by_len;
+        if (s < 1) s = 1;
+        const int64_t tt = cdiv(d->T, tk);
+        if (n_keys > 0 && s + 1 <= smax &&
+            longest_slice_tiles(n_keys, s + 1, tk, tt) < longest_slice_tiles(n_keys, s, tk, tt))
+            s += 1;
     } else {
         const int64_t nrb = cdiv((int64_t)d->T * (d->Hq / d->Hkv), tsw::kValuRows);
         s = (2 * (int64_t)cus) / (d->Hkv * nrb);
