@@ -303,6 +303,39 @@ def test_split_then_merge(n_splits):
     check(o, lse, o_ref, l_ref, TOL["bf16"], "split %d" % n_splits)
 
 
+# Loads are issued in groups of 128 keys (1, 2 or 4 tiles of 128, 64 or 32
+# keys by shape); whole groups run unrolled and the rest of a split's tiles
+# one at a time.  Two splits with an explicit count put 1-3 tiles after the
+# last whole group (plus ragged ends and the tree's tiles in the last split)
+# for every group size.
+GROUP_CASES = [
+    # (T, G, Hkv, tile keys, tiles per split)
+    (13, 1, 1, 128, 3),     # 1 block: 128-key tiles, one tile per group
+    (40, 2, 1, 64, 7),      # 5 blocks: 64-key tiles, two per group
+    (40, 4, 1, 64, 5),      # 10 blocks
+    (40, 5, 1, 32, 11),     # 13 blocks: 32-key tiles, four per group
+    (53, 5, 1, 32, 9),      # 17 blocks
+    (64, 4, 1, 32, 6),      # 16 blocks
+]
+
+
+@pytest.mark.parametrize("T,G,Hkv,tk,tiles", GROUP_CASES)
+@pytest.mark.parametrize("ragged", [0, 5])
+def test_load_group_remainders(T, G, Hkv, tk, tiles, ragged):
+    d = 128
+    npre = 2 * tiles * tk - ragged
+    parent = wl.random_tree_parent(T, T * G + tiles)
+    q = gen((T, G * Hkv, d), 90 + T, torch.bfloat16)
+    k = gen((Hkv, npre + T, d), 91 + T, torch.bfloat16)
+    v = gen((Hkv, npre + T, d), 92 + T, torch.bfloat16)
+    po, pl = tsw.tree_attn_split(q, k, v, parent, npre, 2, impl="mfma")
+    o, lse = tsw.lse_merge(po, pl)
+    torch.cuda.synchronize()
+    o_ref, l_ref = oracle.tree_attn(wl.oracle_view(q), wl.oracle_view(k), wl.oracle_view(v),
+                                    parent, npre, 1 / np.sqrt(d), nthreads=NTHREADS)
+    check(o, lse, o_ref, l_ref, TOL["bf16"], "T=%d G=%d tiles=%d ragged=%d" % (T, G, tiles, ragged))
+
+
 def test_lse_merge_against_oracle():
     rng = np.random.default_rng(5)
     S, R, d = 9, 300, 128
