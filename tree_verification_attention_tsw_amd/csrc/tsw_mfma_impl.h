@@ -76,8 +76,13 @@ struct Shape {
     static constexpr int STAGES_FIT = (160 * 1024 - RESERVE) / STAGE;
     static constexpr int STAGES = 2 * GT;
     static constexpr int RING = STAGES * STAGE;
-    static constexpr int XSLOTS = (KS - 1) * R * NB;   // parked (wave, block) pairs
-    static constexpr int XBYTES = XSLOTS * (8 * 64 * 16 + 32 * 4);
+    // Epilogue exchange: each wave parks, per block, the column blocks the
+    // other KS-1 waves of its row group finish (one f32x4 per lane each),
+    // plus its per-row (m, l).
+    static constexpr int DPW = 8 / KS;                 // column blocks finished per wave
+    static constexpr int XSLOTS = (KS - 1) * R * NB;   // parked blocks' worth of columns
+    static constexpr int XO_BYTES = XSLOTS * 8 * 64 * 16;
+    static constexpr int XBYTES = XO_BYTES + R * NB * KS * 32 * 4;
     // ring (+ index slice) during the loop, the KS exchange afterwards
     static constexpr int LOOP_BYTES = RING + IDX_BYTES;
     static constexpr int SMEM = LOOP_BYTES > XBYTES ? LOOP_BYTES : XBYTES;
@@ -586,25 +591,34 @@ __device__ __forceinline__ void run_wave(const SplitArgs& a, const Ctx& cx) {
 #pragma unroll
     for (int b = 0; b < NBA; ++b) l_run[b] = quad_sum(l_run[b]);
 
-    // Combine the KS key sub-tiles of each row group through LDS.  Block b
-    // of a row group is finished by the wave with ks == b % KS; the other
-    // KS-1 waves park their accumulators for it (lane-major, one f32x4 per
-    // lane) with their per-row (m, l), in slot j = (ks - owner - 1) mod KS.
+    // Combine the KS key sub-tiles of each row group through LDS.  Every
+    // wave of the row group finishes DPW = 8/KS of the 8 column blocks of
+    // each block (wave ks: column blocks ks*DPW ..), so the work is spread
+    // over all KS waves; the others' sums for those columns and every wave's
+    // per-row (m, l) are parked in LDS first.  The partial sums are added in
+    // sub-tile order 0..KS-1 whichever wave finishes, so the result does not
+    // depend on the assignment.
     f32x4* xo = (f32x4*)cx.smem;
-    float* xml = (float*)(cx.smem + S::XSLOTS * 8 * 64 * 16);
-    auto slot = [&](int j, int b) { return (j * S::R + cx.rg) * S::NB + b; };
+    float* xml = (float*)(cx.smem + S::XO_BYTES);
+    // parked column k (0 .. 8-DPW-1) of source wave src: column block db of
+    // src, skipping src's own range
+    auto xo_at = [&](int b, int src, int k) {
+        return xo + ((((cx.rg * S::NB + b) * S::KS + src) * (8 - S::DPW) + k) * 64 + cx.lane);
+    };
+    auto xml_at = [&](int b, int src) { return xml + ((cx.rg * S::NB + b) * S::KS + src) * 32; };
     if constexpr (S::KS > 1) {
         barrier_lds();
 #pragma unroll
         for (int b = 0; b < NBA; ++b) {
-            const int own = b % S::KS;
-            if (own == cx.ks) continue;
-            const int sl = slot((cx.ks - own - 1 + S::KS) % S::KS, b);
 #pragma unroll
-            for (int db = 0; db < 8; ++db) xo[(sl * 8 + db) * 64 + cx.lane] = o[b][db];
+            for (int db = 0; db < 8; ++db) {
+                const int owner = db / S::DPW;
+                if (owner == cx.ks) continue;
+                *xo_at(b, cx.ks, db < cx.ks * S::DPW ? db : db - S::DPW) = o[b][db];
+            }
             if (cx.lj == 0) {
-                xml[sl * 32 + cx.li] = m_run[b];
-                xml[sl * 32 + 16 + cx.li] = l_run[b];
+                xml_at(b, cx.ks)[cx.li] = m_run[b];
+                xml_at(b, cx.ks)[16 + cx.li] = l_run[b];
             }
         }
         barrier_lds();
@@ -612,40 +626,46 @@ __device__ __forceinline__ void run_wave(const SplitArgs& a, const Ctx& cx) {
 
 #pragma unroll
     for (int b = 0; b < NBA; ++b) {
-        if (b % S::KS != cx.ks) continue;
         // per-row weights of the KS partial sums, computed by the lanes that
-        // own row li (own sums first, then the parked ones)
-        float mmax = m_run[b];
+        // own row li, in sub-tile order
+        float mk[S::KS], lk[S::KS];
 #pragma unroll
-        for (int j = 0; j < S::KS - 1; ++j) mmax = fmaxf(mmax, xml[slot(j, b) * 32 + cx.li]);
-        const float w0 = m_run[b] == -INFINITY ? 0.0f : exp2_fast(m_run[b] - mmax);
-        float L = w0 * l_run[b];
-        float wk[S::KS > 1 ? S::KS - 1 : 1];
+        for (int k = 0; k < S::KS; ++k) {
+            if constexpr (S::KS > 1) {
+                mk[k] = xml_at(b, k)[cx.li];
+                lk[k] = xml_at(b, k)[16 + cx.li];
+            } else {
+                mk[k] = m_run[b];
+                lk[k] = l_run[b];
+            }
+        }
+        float mmax = mk[0];
 #pragma unroll
-        for (int j = 0; j < S::KS - 1; ++j) {
-            const float mk = xml[slot(j, b) * 32 + cx.li];
-            wk[j] = mk == -INFINITY ? 0.0f : exp2_fast(mk - mmax);
-            L += wk[j] * xml[slot(j, b) * 32 + 16 + cx.li];
+        for (int k = 1; k < S::KS; ++k) mmax = fmaxf(mmax, mk[k]);
+        float wk[S::KS];
+        float L = 0.0f;
+#pragma unroll
+        for (int k = 0; k < S::KS; ++k) {
+            wk[k] = mk[k] == -INFINITY ? 0.0f : exp2_fast(mk[k] - mmax);
+            L += wk[k] * lk[k];
         }
         const float inv = L > 0.0f ? 1.0f / L : 0.0f;
         const int rbase = (cx.rg + b * S::R) * 16;
-        if (cx.lj == 0 && rbase + cx.li < a.M) {
+        if (cx.ks == 0 && cx.lj == 0 && rbase + cx.li < a.M) {
             const int r = rbase + cx.li;
             const size_t orow = ((size_t)cx.row0 + r / a.G) * a.Hq + cx.g * a.G + r % a.G;
             a.part_lse[orow] = L > 0.0f ? (mmax + __log2f(L)) * kLn2 : -INFINITY;
         }
         // accumulator element i of this lane belongs to row 4*lj + i; the
-        // per-row weights and destinations are formed once, then each
-        // column block reads its parked partner sums together
-        float wq0[4], wq[4][S::KS > 1 ? S::KS - 1 : 1];
+        // per-row weights and destinations are formed once
+        float wq[4][S::KS];
         float* dst[4];
         bool row_ok[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int q = 4 * cx.lj + i;
-            wq0[i] = __shfl(w0 * inv, q);
 #pragma unroll
-            for (int j = 0; j < S::KS - 1; ++j) wq[i][j] = __shfl(wk[j] * inv, q);
+            for (int k = 0; k < S::KS; ++k) wq[i][k] = __shfl(wk[k] * inv, q);
             const int r = rbase + q;
             row_ok[i] = r < a.M;
             const int rr = row_ok[i] ? r : rbase;
@@ -654,14 +674,13 @@ __device__ __forceinline__ void run_wave(const SplitArgs& a, const Ctx& cx) {
         }
 #pragma unroll
         for (int db = 0; db < 8; ++db) {
-            float acc[4];
+            if (db / S::DPW != cx.ks) continue;
+            float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-            for (int i = 0; i < 4; ++i) acc[i] = o[b][db][i] * wq0[i];
+            for (int k = 0; k < S::KS; ++k) {
+                const f32x4 x = k == cx.ks ? o[b][db] : *xo_at(b, k, db < k * S::DPW ? db : db - S::DPW);
 #pragma unroll
-            for (int j = 0; j < S::KS - 1; ++j) {
-                const f32x4 x = xo[(slot(j, b) * 8 + db) * 64 + cx.lane];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) acc[i] += wq[i][j] * x[i];
+                for (int i = 0; i < 4; ++i) acc[i] += wq[i][k] * x[i];
             }
 #pragma unroll
             for (int i = 0; i < 4; ++i)
