@@ -214,10 +214,19 @@ __global__ __launch_bounds__(64) void accept_walk(const AcceptArgs a, const Acce
     const bool live = t < a.T;
     int tok = 0;
     if (live) {
+        // the fold is order-free (largest value, lowest index among equal
+        // ones; NaN never wins), so the slices' partials are loaded U at a
+        // time before they are folded: one memory round trip per U slices
+        constexpr int U = 16;
         Best b{-INFINITY, INT_MAX};
-        for (int c = 0; c < a.n_chunks; ++c) {
-            const AcceptPartial p = part[(int64_t)t * a.n_chunks + c];
-            b = better(b, Best{p.v, p.i});
+        const AcceptPartial* row = part + (int64_t)t * a.n_chunks;
+        for (int c0 = 0; c0 < a.n_chunks; c0 += U) {
+            AcceptPartial p[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                p[u] = c0 + u < a.n_chunks ? row[c0 + u] : AcceptPartial{-INFINITY, INT_MAX};
+#pragma unroll
+            for (int u = 0; u < U; ++u) b = better(b, Best{p[u].v, p[u].i});
         }
         // all-NaN rows leave no index: report token 0 (NaN logits are outside
         // the contract)
