@@ -1,6 +1,6 @@
 // Matrix-core split kernel for tree-verification attention (gfx950, bf16,
-// head dim 128) -- template code, instantiated per row-group shape in
-// tsw_mfma_r*.hip.
+// head dim 128) -- template code, instantiated once per shape by
+// tsw_mfma_inst.hip.
 //
 // One work-group per (split, kv head): it streams a contiguous slice of that
 // head's key list once (prefix keys, then -- in the last split -- the tree's
@@ -26,8 +26,10 @@
 //     query rows on N, so every lane owns one query row of each block.
 //   * O += P V on the same instruction (queries on rows); V operands come
 //     straight from row-major LDS through ds_read_b64_tr_b16.
-//   * Blocks are pipelined: the Q K products of block b+1 share a basic block
-//     with the exponentials of block b, so matrix and vector work overlap.
+//   * Four-wave shapes pipeline blocks (the Q K products of block b+1 share
+//     a basic block with the exponentials of block b); eight-wave shapes run
+//     Q K of all blocks, the exponentials, then P V, and leave the overlap to
+//     the SIMD's other wave.
 //
 // Softmax without a running maximum.  The fast pass exponentiates scores
 // directly, p = 2^(s * scale * log2 e), and accumulates O and l = sum p.
