@@ -336,17 +336,31 @@ def test_load_group_remainders(T, G, Hkv, tk, tiles, ragged):
     check(o, lse, o_ref, l_ref, TOL["bf16"], "T=%d G=%d tiles=%d ragged=%d" % (T, G, tiles, ragged))
 
 
-def test_lse_merge_against_oracle():
-    rng = np.random.default_rng(5)
-    S, R, d = 9, 300, 128
+@pytest.mark.parametrize("S,R,d,misaligned", [(9, 300, 128, False), (9, 301, 128, False), (40, 7, 128, False),
+                                             (17, 301, 128, True), (9, 300, 64, False)])
+def test_lse_merge_against_oracle(S, R, d, misaligned):
+    """Both merge kernels: two rows per wavefront (d = 128, 16-byte aligned;
+    an odd row count leaves the last wavefront half empty; more than 32
+    splits take a second round of LSE lanes) and one row per wavefront (an
+    output 4 bytes off 16-byte alignment, d = 64).  Empty splits and rows
+    whose every split is empty included."""
+    rng = np.random.default_rng(5 + S + R)
     po = rng.standard_normal((S, R, d)).astype(np.float32)
     pl = (rng.standard_normal((S, R)) * 5).astype(np.float32)
     pl[2] = -np.inf
-    pl[5, :100] = -np.inf
-    o, lse = tsw.lse_merge(torch.from_numpy(po).cuda(), torch.from_numpy(pl).cuda())
+    pl[5, :R // 3] = -np.inf
+    pl[:, R - 1] = -np.inf
+    out = None
+    if misaligned:
+        buf = torch.empty(R * d + 1, dtype=torch.float32, device="cuda")
+        out = (buf[1:].view(R, d), torch.empty(R, dtype=torch.float32, device="cuda"))
+    o, lse = tsw.lse_merge(torch.from_numpy(po).cuda(), torch.from_numpy(pl).cuda(), out=out)
     torch.cuda.synchronize()
     o_ref, l_ref = oracle.lse_merge(po.astype(np.float64), pl.astype(np.float64))
-    check(o, lse, o_ref, l_ref, 1e-5, "merge")
+    # the row with every split empty: LSE -inf and a zero row on both sides
+    assert l_ref[R - 1] == -np.inf and np.all(o_ref[R - 1] == 0.0)
+    assert float(lse[R - 1]) == -np.inf and bool(torch.all(o[R - 1] == 0.0))
+    check(o[:R - 1], lse[:R - 1], o_ref[:R - 1], l_ref[:R - 1], 1e-5, "merge S=%d R=%d d=%d" % (S, R, d))
 
 
 def test_deterministic():

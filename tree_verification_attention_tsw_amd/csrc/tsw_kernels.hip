@@ -257,6 +257,74 @@ __global__ __launch_bounds__(256) void lse_merge(int n_splits, int64_t n_rows, c
     merge_row<D, CH>(n_splits, n_rows, r, r, part_o, part_lse, o, lse);
 }
 
+// One sequence, head dim 128: two rows per wavefront, 32 lanes per row, four
+// consecutive columns per lane, so each load instruction moves the two
+// rows' 1 KB of a split's partials (rows r and r+1 are adjacent).  Lanes of
+// a half hold the split LSEs (32 at a time); the reductions stay inside the
+// half.  Same arithmetic as merge_row, with 32-lane instead of 64-lane
+// reduction trees.
+template <int CH>
+__global__ __launch_bounds__(256) void lse_merge_pairs(int n_splits, int64_t n_rows, const float* __restrict__ part_o,
+                                                       const float* __restrict__ part_lse, float* __restrict__ o,
+                                                       float* __restrict__ lse) {
+    constexpr float kL2e = 1.44269504088896340736f;
+    const int lane = threadIdx.x & 63, h = lane >> 5, l = lane & 31;
+    const int64_t r = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * 2 + h;
+    if (r - h >= n_rows) return;                     // the whole wave is past the end (uniform)
+    const bool valid = r < n_rows;
+    const int64_t rl = valid ? r : n_rows - 1;       // loads stay inside the partials
+    const f32x4* src = (const f32x4*)(part_o + rl * 128) + l;
+    const int64_t sstride = n_rows * 128 / 4;        // f32x4 elements between splits
+
+    f32x4 x[CH];
+#pragma unroll
+    for (int j = 0; j < CH; ++j) x[j] = src[(int64_t)(j < n_splits ? j : n_splits - 1) * sstride];
+    const float ls0 = l < n_splits ? part_lse[(int64_t)l * n_rows + rl] : -INFINITY;
+
+    float mx = ls0;
+    for (int s0 = 32; s0 < n_splits; s0 += 32)
+        if (s0 + l < n_splits) mx = fmaxf(mx, part_lse[(int64_t)(s0 + l) * n_rows + rl]);
+#pragma unroll
+    for (int m = 16; m >= 1; m >>= 1) mx = xor_max(mx, m);
+    const bool empty = mx == -INFINITY;
+    float sum = ls0 == -INFINITY ? 0.0f : exp2f((ls0 - mx) * kL2e);
+    for (int s0 = 32; s0 < n_splits; s0 += 32)
+        if (s0 + l < n_splits) {
+            const float ls = part_lse[(int64_t)(s0 + l) * n_rows + rl];
+            sum += ls == -INFINITY ? 0.0f : exp2f((ls - mx) * kL2e);
+        }
+#pragma unroll
+    for (int m = 16; m >= 1; m >>= 1) sum = xor_sum(sum, m);
+    const float L = empty ? -INFINITY : mx + logf(sum);
+
+    f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int s0 = 0; s0 < n_splits; s0 += 32) {
+        // weight of split s0 + l (0 past the end, and for an empty row)
+        const float ls = s0 == 0 ? ls0 : (s0 + l < n_splits ? part_lse[(int64_t)(s0 + l) * n_rows + rl] : -INFINITY);
+        const float wl = (empty || ls == -INFINITY) ? 0.0f : exp2f((ls - L) * kL2e);
+        const int ng = n_splits - s0 < 32 ? n_splits - s0 : 32;
+        for (int c0 = 0; c0 < ng; c0 += CH) {
+            if (s0 + c0 > 0) {
+#pragma unroll
+                for (int j = 0; j < CH; ++j) {
+                    const int sp = s0 + c0 + j < n_splits ? s0 + c0 + j : n_splits - 1;
+                    x[j] = src[(int64_t)sp * sstride];
+                }
+            }
+#pragma unroll
+            for (int j = 0; j < CH; ++j) {
+                const float wj = __shfl(wl, (h << 5) + c0 + j);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) acc[e] = fmaf(wj, x[j][e], acc[e]);
+            }
+        }
+    }
+    if (valid) {
+        *(f32x4*)(o + r * 128 + 4 * l) = acc;
+        if (l == 0) lse[r] = L;
+    }
+}
+
 // Several sequences, each with its own run of splits of rows_per_seg rows.
 template <int D, int CH>
 __global__ __launch_bounds__(256) void lse_merge_segs(const MergeSegs segs, int64_t n_rows,
@@ -351,7 +419,18 @@ hipError_t launch_lse_merge(int n_splits, int64_t n_rows, int d, const float* pa
         const dim3 grid((unsigned)((n_rows + 3) / 4));
 #define TSW_MERGE(D_, CH_) \
     hipLaunchKernelGGL((lse_merge<D_, CH_>), grid, dim3(256), 0, stream, n_splits, n_rows, part_o, part_lse, o, lse)
-        if (d == 128) {
+        // the paired kernel moves 16-byte pieces: partials and output must
+        // be 16-byte aligned (any alignment takes the row-per-wave kernel)
+        const bool aligned16 = (((uintptr_t)part_o | (uintptr_t)o) & 15) == 0;
+        if (d == 128 && aligned16) {
+            const dim3 pgrid((unsigned)((n_rows + 7) / 8));
+#define TSW_MERGE_PAIRS(CH_) \
+    hipLaunchKernelGGL((lse_merge_pairs<CH_>), pgrid, dim3(256), 0, stream, n_splits, n_rows, part_o, part_lse, o, lse)
+            if (n_splits <= 8) TSW_MERGE_PAIRS(8);
+            else if (n_splits <= 16) TSW_MERGE_PAIRS(16);
+            else TSW_MERGE_PAIRS(32);
+#undef TSW_MERGE_PAIRS
+        } else if (d == 128) {
             if (n_splits <= 8) TSW_MERGE(128, 8);
             else if (n_splits <= 16) TSW_MERGE(128, 16);
             else TSW_MERGE(128, 32);
