@@ -93,6 +93,12 @@ def test_paged_random_tree_T64():
     check_batch([2000, 4500], 64, 8, 2, 32, 5, parent=wl.random_tree_parent(64, 5))
 
 
+def test_paged_odd_rows_per_sequence():
+    # 13 nodes x 5 query heads = 65 rows per sequence: the segmented merge
+    # cannot pair rows across sequences and takes its row-per-wave kernel
+    check_batch([1500, 700, 2049], 13, 5, 1, 16, 8)
+
+
 def test_paged_many_sequences():
     check_batch([400 + 137 * b for b in range(16)], 13, 32, 8, 16, 6)
 

@@ -257,40 +257,38 @@ __global__ __launch_bounds__(256) void lse_merge(int n_splits, int64_t n_rows, c
     merge_row<D, CH>(n_splits, n_rows, r, r, part_o, part_lse, o, lse);
 }
 
-// One sequence, head dim 128: two rows per wavefront, 32 lanes per row, four
-// consecutive columns per lane, so each load instruction moves the two
-// rows' 1 KB of a split's partials (rows r and r+1 are adjacent).  Lanes of
-// a half hold the split LSEs (32 at a time); the reductions stay inside the
-// half.  Same arithmetic as merge_row, with 32-lane instead of 64-lane
-// reduction trees.
+// Head dim 128, two rows per wavefront: 32 lanes per row, four consecutive
+// columns per lane, so each load instruction moves the two rows' 1 KB of a
+// split's partials (the rows are adjacent and in the same run of splits).
+// Lanes of a half hold the split LSEs (32 at a time) and the reductions stay
+// inside the half.  Same arithmetic as merge_row, with 32-lane instead of
+// 64-lane reduction trees.  rr: the row within its run (blocks of `stride`
+// rows from part_o / part_lse); r: the output row; valid: r is a real row
+// (the half past an odd row count only loads a valid row and stores nothing).
 template <int CH>
-__global__ __launch_bounds__(256) void lse_merge_pairs(int n_splits, int64_t n_rows, const float* __restrict__ part_o,
-                                                       const float* __restrict__ part_lse, float* __restrict__ o,
-                                                       float* __restrict__ lse) {
+__device__ __forceinline__ void merge_pair(int n_splits, int64_t stride, int64_t rr, int64_t r, bool valid,
+                                           const float* __restrict__ part_o, const float* __restrict__ part_lse,
+                                           float* __restrict__ o, float* __restrict__ lse) {
     constexpr float kL2e = 1.44269504088896340736f;
     const int lane = threadIdx.x & 63, h = lane >> 5, l = lane & 31;
-    const int64_t r = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * 2 + h;
-    if (r - h >= n_rows) return;                     // the whole wave is past the end (uniform)
-    const bool valid = r < n_rows;
-    const int64_t rl = valid ? r : n_rows - 1;       // loads stay inside the partials
-    const f32x4* src = (const f32x4*)(part_o + rl * 128) + l;
-    const int64_t sstride = n_rows * 128 / 4;        // f32x4 elements between splits
+    const f32x4* src = (const f32x4*)(part_o + rr * 128) + l;
+    const int64_t sstride = stride * 128 / 4;        // f32x4 elements between splits
 
     f32x4 x[CH];
 #pragma unroll
     for (int j = 0; j < CH; ++j) x[j] = src[(int64_t)(j < n_splits ? j : n_splits - 1) * sstride];
-    const float ls0 = l < n_splits ? part_lse[(int64_t)l * n_rows + rl] : -INFINITY;
+    const float ls0 = l < n_splits ? part_lse[(int64_t)l * stride + rr] : -INFINITY;
 
     float mx = ls0;
     for (int s0 = 32; s0 < n_splits; s0 += 32)
-        if (s0 + l < n_splits) mx = fmaxf(mx, part_lse[(int64_t)(s0 + l) * n_rows + rl]);
+        if (s0 + l < n_splits) mx = fmaxf(mx, part_lse[(int64_t)(s0 + l) * stride + rr]);
 #pragma unroll
     for (int m = 16; m >= 1; m >>= 1) mx = xor_max(mx, m);
     const bool empty = mx == -INFINITY;
     float sum = ls0 == -INFINITY ? 0.0f : exp2f((ls0 - mx) * kL2e);
     for (int s0 = 32; s0 < n_splits; s0 += 32)
         if (s0 + l < n_splits) {
-            const float ls = part_lse[(int64_t)(s0 + l) * n_rows + rl];
+            const float ls = part_lse[(int64_t)(s0 + l) * stride + rr];
             sum += ls == -INFINITY ? 0.0f : exp2f((ls - mx) * kL2e);
         }
 #pragma unroll
@@ -300,7 +298,7 @@ __global__ __launch_bounds__(256) void lse_merge_pairs(int n_splits, int64_t n_r
     f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
     for (int s0 = 0; s0 < n_splits; s0 += 32) {
         // weight of split s0 + l (0 past the end, and for an empty row)
-        const float ls = s0 == 0 ? ls0 : (s0 + l < n_splits ? part_lse[(int64_t)(s0 + l) * n_rows + rl] : -INFINITY);
+        const float ls = s0 == 0 ? ls0 : (s0 + l < n_splits ? part_lse[(int64_t)(s0 + l) * stride + rr] : -INFINITY);
         const float wl = (empty || ls == -INFINITY) ? 0.0f : exp2f((ls - L) * kL2e);
         const int ng = n_splits - s0 < 32 ? n_splits - s0 : 32;
         for (int c0 = 0; c0 < ng; c0 += CH) {
@@ -323,6 +321,37 @@ __global__ __launch_bounds__(256) void lse_merge_pairs(int n_splits, int64_t n_r
         *(f32x4*)(o + r * 128 + 4 * l) = acc;
         if (l == 0) lse[r] = L;
     }
+}
+
+// One sequence: n_splits blocks of n_rows rows, two rows per wavefront.
+template <int CH>
+__global__ __launch_bounds__(256) void lse_merge_pairs(int n_splits, int64_t n_rows, const float* __restrict__ part_o,
+                                                       const float* __restrict__ part_lse, float* __restrict__ o,
+                                                       float* __restrict__ lse) {
+    const int h = (threadIdx.x >> 5) & 1;
+    const int64_t r = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * 2 + h;
+    if (r - h >= n_rows) return;                     // the whole wave is past the end (uniform)
+    const bool valid = r < n_rows;
+    const int64_t rl = valid ? r : n_rows - 1;
+    merge_pair<CH>(n_splits, n_rows, rl, r, valid, part_o, part_lse, o, lse);
+}
+
+// Several sequences with an even number of rows each (so a wavefront's two
+// rows share a run of splits), two rows per wavefront.
+template <int CH>
+__global__ __launch_bounds__(256) void lse_merge_segs_pairs(const MergeSegs segs, int64_t n_rows,
+                                                            const float* __restrict__ part_o,
+                                                            const float* __restrict__ part_lse,
+                                                            float* __restrict__ o, float* __restrict__ lse) {
+    const int h = (threadIdx.x >> 5) & 1;
+    const int64_t r0 = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * 2;
+    if (r0 >= n_rows) return;                        // uniform
+    const int64_t r = r0 + h;                        // r0 even, rows_per_seg even: same run
+    const int seg = (int)((uint32_t)r0 / (uint32_t)segs.rows_per_seg);
+    const int64_t rr = r - (int64_t)seg * segs.rows_per_seg;
+    const int64_t first = (int64_t)segs.base[seg] * segs.rows_per_seg;
+    merge_pair<CH>(segs.base[seg + 1] - segs.base[seg], segs.rows_per_seg, rr, r, r < n_rows, part_o + first * 128,
+                   part_lse + first, o, lse);
 }
 
 // Several sequences, each with its own run of splits of rows_per_seg rows.
@@ -401,6 +430,21 @@ hipError_t launch_lse_merge_segs(const MergeSegs& segs, int64_t n_rows, const fl
     int most = 1;
     for (int b = 0; b < segs.n_seg; ++b)
         most = segs.base[b + 1] - segs.base[b] > most ? segs.base[b + 1] - segs.base[b] : most;
+    // two rows per wavefront when a wavefront's rows always share a run
+    // (even rows per sequence) and the 16-byte pieces are aligned
+    if (segs.rows_per_seg % 2 == 0 && (((uintptr_t)part_o | (uintptr_t)o) & 15) == 0) {
+        const dim3 pgrid((unsigned)((n_rows + 7) / 8));
+        if (most <= 8)
+            hipLaunchKernelGGL((lse_merge_segs_pairs<8>), pgrid, dim3(256), 0, stream, segs, n_rows, part_o, part_lse,
+                               o, lse);
+        else if (most <= 16)
+            hipLaunchKernelGGL((lse_merge_segs_pairs<16>), pgrid, dim3(256), 0, stream, segs, n_rows, part_o,
+                               part_lse, o, lse);
+        else
+            hipLaunchKernelGGL((lse_merge_segs_pairs<32>), pgrid, dim3(256), 0, stream, segs, n_rows, part_o,
+                               part_lse, o, lse);
+        return hipGetLastError();
+    }
     if (most <= 8)
         hipLaunchKernelGGL((lse_merge_segs<128, 8>), grid, dim3(256), 0, stream, segs, n_rows, part_o, part_lse, o, lse);
     else if (most <= 16)
