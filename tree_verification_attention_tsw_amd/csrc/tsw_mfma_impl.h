@@ -63,9 +63,9 @@ struct Shape {
     static constexpr int ROWB = 256;                // bytes per K or V row
     static constexpr int STAGE = 2 * TK * ROWB;     // one K tile + one V tile
     static constexpr int NI = TK / (2 * WAVES);     // DMA instructions per wave per tile
-    // LDS beyond the ring: row-sum pool and votes, the tree mask, and for
-    // the gather and paged variants the staged index or page-table slice.
-    static constexpr int POOL = WAVES * NB * 16 * 4 + WAVES * 4;
+    // LDS beyond the ring: the work-group vote, the tree mask, and for the
+    // gather and paged variants the staged index or page-table slice.
+    static constexpr int POOL = WAVES * 4;            // the work-group vote
     static constexpr int MASK_BYTES = 64 * 8;
     static constexpr int IDX_BYTES = MODE_ != kModeContig ? kGatherChunkMax * 4 : 0;
     static constexpr int RESERVE = ((POOL + MASK_BYTES + 255) & ~255) + IDX_BYTES;
@@ -537,35 +537,70 @@ __device__ __forceinline__ void run_wave(const SplitArgs& a, const Ctx& cx) {
 
     pass(std::integral_constant<int, FAST>{});
 
+    // The KS key sub-tiles of each row group meet through LDS.  Every wave
+    // of the row group finishes DPW = 8/KS of the 8 column blocks of each
+    // block (wave ks: column blocks ks*DPW ..), so the work is spread over
+    // all KS waves; the others' sums for those columns and every wave's
+    // per-row (m, l) are parked in LDS first (the exchange region overlaps
+    // the ring, hence the barrier before).  The partial sums are added in
+    // sub-tile order 0..KS-1 whichever wave finishes, so the result does not
+    // depend on the assignment.
+    f32x4* xo = (f32x4*)cx.smem;
+    float* xml = (float*)(cx.smem + S::XO_BYTES);
+    // parked column k (0 .. 8-DPW-1) of source wave src: column block db of
+    // src, skipping src's own range
+    auto xo_at = [&](int b, int src, int k) {
+        return xo + ((((cx.rg * S::NB + b) * S::KS + src) * (8 - S::DPW) + k) * 64 + cx.lane);
+    };
+    auto xml_at = [&](int b, int src) { return xml + ((cx.rg * S::NB + b) * S::KS + src) * 32; };
+    auto park = [&]() {
+        // row sums: each lane summed its own keys; add the four lane groups
+#pragma unroll
+        for (int b = 0; b < NBA; ++b) l_run[b] = quad_sum(l_run[b]);
+        if constexpr (S::KS > 1) {
+            barrier_lds();
+#pragma unroll
+            for (int b = 0; b < NBA; ++b) {
+#pragma unroll
+                for (int db = 0; db < 8; ++db) {
+                    const int owner = db / S::DPW;
+                    if (owner == cx.ks) continue;
+                    *xo_at(b, cx.ks, db < cx.ks * S::DPW ? db : db - S::DPW) = o[b][db];
+                }
+                if (cx.lj == 0) {
+                    xml_at(b, cx.ks)[cx.li] = m_run[b];
+                    xml_at(b, cx.ks)[16 + cx.li] = l_run[b];
+                }
+            }
+            barrier_lds();
+        }
+    };
+    park();
+
     // Accept the fast pass only if, for every row of the work-group, the sum
-    // of p over all its key sub-tiles is finite and not vanishing (a split
-    // with any tile gives every row at least one visible key), and the
-    // accumulators are finite.  Row sums are pooled through LDS first: one
-    // wave's share of a row may legitimately hold no visible key.
-    float* pool = (float*)(cx.smem + S::SMEM);      // [waves][NB][16]
-    int* votes = (int*)(pool + S::WAVES * S::NB * 16);
+    // of p over all its key sub-tiles (from the parked sums: one wave's share
+    // of a row may legitimately hold no visible key) is finite and not
+    // vanishing (a split with any tile gives every row at least one visible
+    // key), and the accumulators are finite.
+    int* votes = (int*)(cx.smem + S::SMEM);
     bool bad = false;
-    float lq[NBA];
 #pragma unroll
     for (int b = 0; b < NBA; ++b) {
-        lq[b] = quad_sum(l_run[b]);
         float os = 0.0f;
 #pragma unroll
         for (int db = 0; db < 8; ++db) os += (o[b][db][0] + o[b][db][1]) + (o[b][db][2] + o[b][db][3]);
         bad = bad || !(os - os == 0.0f);
     }
-    barrier_lds();
-    if (cx.lj == 0) {
-#pragma unroll
-        for (int b = 0; b < NBA; ++b) pool[(cx.w * S::NB + b) * 16 + cx.li] = lq[b];
-    }
-    barrier_lds();
     if (n > 0) {
 #pragma unroll
         for (int b = 0; b < NBA; ++b) {
             float L = 0.0f;
+            if constexpr (S::KS > 1) {
 #pragma unroll
-            for (int k2 = 0; k2 < S::KS; ++k2) L += pool[((cx.rg * S::KS + k2) * S::NB + b) * 16 + cx.li];
+                for (int k2 = 0; k2 < S::KS; ++k2) L += xml_at(b, k2)[16 + cx.li];
+            } else {
+                L = l_run[b];                        // every lane (li, lj) holds row li's sum
+            }
             bad = bad || !(L >= kMinRowSum && L <= 3.0e38f);
         }
     }
@@ -587,43 +622,7 @@ __device__ __forceinline__ void run_wave(const SplitArgs& a, const Ctx& cx) {
             for (int db = 0; db < 8; ++db) o[b][db] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
         pass(std::integral_constant<int, EXACT>{});
-    }
-
-    // Row sums: each lane summed its own keys; add the four lane groups.
-#pragma unroll
-    for (int b = 0; b < NBA; ++b) l_run[b] = quad_sum(l_run[b]);
-
-    // Combine the KS key sub-tiles of each row group through LDS.  Every
-    // wave of the row group finishes DPW = 8/KS of the 8 column blocks of
-    // each block (wave ks: column blocks ks*DPW ..), so the work is spread
-    // over all KS waves; the others' sums for those columns and every wave's
-    // per-row (m, l) are parked in LDS first.  The partial sums are added in
-    // sub-tile order 0..KS-1 whichever wave finishes, so the result does not
-    // depend on the assignment.
-    f32x4* xo = (f32x4*)cx.smem;
-    float* xml = (float*)(cx.smem + S::XO_BYTES);
-    // parked column k (0 .. 8-DPW-1) of source wave src: column block db of
-    // src, skipping src's own range
-    auto xo_at = [&](int b, int src, int k) {
-        return xo + ((((cx.rg * S::NB + b) * S::KS + src) * (8 - S::DPW) + k) * 64 + cx.lane);
-    };
-    auto xml_at = [&](int b, int src) { return xml + ((cx.rg * S::NB + b) * S::KS + src) * 32; };
-    if constexpr (S::KS > 1) {
-        barrier_lds();
-#pragma unroll
-        for (int b = 0; b < NBA; ++b) {
-#pragma unroll
-            for (int db = 0; db < 8; ++db) {
-                const int owner = db / S::DPW;
-                if (owner == cx.ks) continue;
-                *xo_at(b, cx.ks, db < cx.ks * S::DPW ? db : db - S::DPW) = o[b][db];
-            }
-            if (cx.lj == 0) {
-                xml_at(b, cx.ks)[cx.li] = m_run[b];
-                xml_at(b, cx.ks)[16 + cx.li] = l_run[b];
-            }
-        }
-        barrier_lds();
+        park();
     }
 
 #pragma unroll
@@ -701,7 +700,7 @@ __global__ __launch_bounds__(W * 64, 1) void split_mfma(const SplitArgs a) {
     constexpr int MASK_OFF = (SMEM + S::POOL + 7) & ~7;
     static_assert(MASK_OFF + 64 * 8 <= 160 * 1024, "LDS budget");
     static_assert(S::NI >= 1 && (S::TK / 2) % S::WAVES == 0, "tile / wave split");
-    // + row-sum pool and votes used once after the fast pass, + the tree mask
+    // + the votes used once after the fast pass, + the tree mask
     // (read from LDS in masked tiles: a per-lane read of the kernel
     // arguments would be a vector memory load, and waiting for it would
     // drain the K/V ring)
