@@ -93,6 +93,11 @@ def test_paged_random_tree_T64():
     check_batch([2000, 4500], 64, 8, 2, 32, 5, parent=wl.random_tree_parent(64, 5))
 
 
+def test_paged_twenty_query_blocks():
+    # 64 nodes x 5 query heads = 320 rows per kv head (the 17-24 block shape)
+    check_batch([3000, 1700], 64, 20, 4, 16, 9, parent=wl.random_tree_parent(64, 9))
+
+
 def test_paged_odd_rows_per_sequence():
     # 13 nodes x 5 query heads = 65 rows per sequence: the segmented merge
     # cannot pair rows across sequences and takes its row-per-wave kernel

@@ -111,6 +111,7 @@ def check_selection(imp_gpu, imp_ref, idx, n_prefix, n_keep, n_idx):
 @pytest.mark.parametrize("T,Hq,Hkv,d,n_prefix,n_keep,n_idx,dtype", [
     (40, 32, 8, 128, 102400, 128, 4096, "bf16"),  # root scores from the split kernel
     (40, 40, 8, 128, 20003, 128, 4096, "bf16"),   # ragged prefix end, G = 5
+    (64, 20, 4, 128, 7001, 64, 1000, "bf16"),     # 320 rows per kv head: 20 query blocks
     (13, 32, 32, 128, 9000, 64, 1000, "bf16"),    # G = 1
     (4, 32, 1, 128, 5000, 16, 300, "bf16"),       # G = 32: importance from K
     (13, 4, 4, 64, 3000, 16, 500, "f32"),         # vector-ALU verification
