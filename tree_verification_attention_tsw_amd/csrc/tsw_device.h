@@ -84,6 +84,16 @@ __device__ __forceinline__ bf16x4 ds_read_tr16_b64_at(const char* p) {
     return r;
 }
 
+// Wait until at most N LDS operations are outstanding.  LDS reads complete
+// in issue order, so with N = the number of LDS reads issued after x and y,
+// x and y have landed (any other outstanding LDS operation only makes the
+// wait stricter).
+template <int N>
+__device__ __forceinline__ void lds_wait_n(bf16x4& x, bf16x4& y) {
+    static_assert(N >= 0 && N <= 15, "lgkmcnt range");
+    asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(x), "+v"(y) : "i"(N));
+}
+
 // Wait for every outstanding LDS read (and scalar load); tying the values
 // keeps their uses after the wait.
 __device__ __forceinline__ void lds_wait(bf16x4& x, bf16x4& y) {

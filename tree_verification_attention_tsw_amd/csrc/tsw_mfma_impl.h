@@ -46,6 +46,7 @@
 #include "tsw_device.h"
 #include "tsw_internal.h"
 
+
 namespace tsw {
 namespace mfma {
 
@@ -371,10 +372,6 @@ __device__ __forceinline__ void tile_pv_shared(const SplitArgs& a, const Ctx& cx
         }
     }
     if constexpr (EMIT) emit_root<S, MASKED>(a, cx, tt, sc[0]);
-    bf16x8 pb[NBA];
-#pragma unroll
-    for (int b = 0; b < NBA; ++b)
-        softmax_block<SHIFT>(sc[b], c, (SHIFT && m[b] != -INFINITY) ? m[b] : 0.0f, l[b], pb[b]);
     // V rows are addressed from the K stage: the stage offset, the V tile
     // and the second 16-row half (same swizzle) are constant offsets of the
     // read.
@@ -383,17 +380,56 @@ __device__ __forceinline__ void tile_pv_shared(const SplitArgs& a, const Ctx& cx
     const int tsel = (cx.li >> 1) & 1;
     const char* vrow0 = Ks + trow0 * S::ROWB + 8 * (cx.li & 1);
     const int sw0 = swz(trow0) ^ tsel;
-    // V operands for column block db+1 are read while the products of block
-    // db run.
-    bf16x4 c0 = ds_read_tr16_b64_at<VOFF>(vrow0 + 16 * (0 ^ sw0));
-    bf16x4 c1 = ds_read_tr16_b64_at<VOFF + 16 * S::ROWB>(vrow0 + 16 * (0 ^ sw0));
+    // V operands go through a window of VW column blocks (two transposed
+    // reads each).  The first VW blocks are read before the exponentials, so
+    // their latency hides under them; each later block is read as the window
+    // moves, and block db waits only for its own two reads.  Deeper windows
+    // push the three-block waves of the larger shapes into register spills,
+    // so those keep a window of one block read after the exponentials.
+    constexpr int VW = NBA >= 3 ? (S::R == 8 ? 1 : 2) : 4;
+    if constexpr (VW == 1) {
+        bf16x8 pb[NBA];
+#pragma unroll
+        for (int b = 0; b < NBA; ++b)
+            softmax_block<SHIFT>(sc[b], c, (SHIFT && m[b] != -INFINITY) ? m[b] : 0.0f, l[b], pb[b]);
+        bf16x4 c0 = ds_read_tr16_b64_at<VOFF>(vrow0 + 16 * (0 ^ sw0));
+        bf16x4 c1 = ds_read_tr16_b64_at<VOFF + 16 * S::ROWB>(vrow0 + 16 * (0 ^ sw0));
+#pragma unroll
+        for (int db = 0; db < 8; ++db) {
+            lds_wait(c0, c1);
+            const bf16x8 vop = __builtin_shufflevector(c0, c1, 0, 1, 2, 3, 4, 5, 6, 7);
+            if (db + 1 < 8) {
+                c0 = ds_read_tr16_b64_at<VOFF>(vrow0 + 16 * ((2 * (db + 1)) ^ sw0));
+                c1 = ds_read_tr16_b64_at<VOFF + 16 * S::ROWB>(vrow0 + 16 * ((2 * (db + 1)) ^ sw0));
+            }
+#pragma unroll
+            for (int b = 0; b < NBA; ++b)
+                o[b][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pb[b], vop, o[b][db], 0, 0, 0);
+        }
+        return;
+    }
+    bf16x4 va[8], vb[8];
+#pragma unroll
+    for (int db = 0; db < VW; ++db) {
+        va[db] = ds_read_tr16_b64_at<VOFF>(vrow0 + 16 * ((2 * db) ^ sw0));
+        vb[db] = ds_read_tr16_b64_at<VOFF + 16 * S::ROWB>(vrow0 + 16 * ((2 * db) ^ sw0));
+    }
+    bf16x8 pb[NBA];
+#pragma unroll
+    for (int b = 0; b < NBA; ++b)
+        softmax_block<SHIFT>(sc[b], c, (SHIFT && m[b] != -INFINITY) ? m[b] : 0.0f, l[b], pb[b]);
 #pragma unroll
     for (int db = 0; db < 8; ++db) {
-        lds_wait(c0, c1);
-        const bf16x8 vop = __builtin_shufflevector(c0, c1, 0, 1, 2, 3, 4, 5, 6, 7);
-        if (db + 1 < 8) {
-            c0 = ds_read_tr16_b64_at<VOFF>(vrow0 + 16 * ((2 * (db + 1)) ^ sw0));
-            c1 = ds_read_tr16_b64_at<VOFF + 16 * S::ROWB>(vrow0 + 16 * ((2 * (db + 1)) ^ sw0));
+        // LDS reads issued after block db's: the window's later blocks
+        constexpr int after_cap = 2 * (VW - 1);
+        if (7 - db >= VW - 1) lds_wait_n<after_cap>(va[db], vb[db]);
+        else if (7 - db == 2) lds_wait_n<4>(va[db], vb[db]);
+        else if (7 - db == 1) lds_wait_n<2>(va[db], vb[db]);
+        else lds_wait_n<0>(va[db], vb[db]);
+        const bf16x8 vop = __builtin_shufflevector(va[db], vb[db], 0, 1, 2, 3, 4, 5, 6, 7);
+        if (db + VW < 8) {
+            va[db + VW] = ds_read_tr16_b64_at<VOFF>(vrow0 + 16 * ((2 * (db + VW)) ^ sw0));
+            vb[db + VW] = ds_read_tr16_b64_at<VOFF + 16 * S::ROWB>(vrow0 + 16 * ((2 * (db + VW)) ^ sw0));
         }
 #pragma unroll
         for (int b = 0; b < NBA; ++b) o[b][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pb[b], vop, o[b][db], 0, 0, 0);
@@ -514,12 +550,42 @@ __device__ __forceinline__ void run_wave(const SplitArgs& a, const Ctx& cx) {
         int t = 0;
         // Whole groups of full tiles: the group's tiles are unrolled so
         // their stage offsets are constants.
+        // The next group goes out in two halves, at the start of this group
+        // and half-way through it (32 KB per work-group at a time): a whole
+        // group of 64 KB at once exceeds the LDS-DMA requests a CU keeps in
+        // flight, and the issuing waves would stall until earlier requests
+        // drain.
+        constexpr int HALF = S::GT >= 2 ? S::GT / 2 : 1;
+        auto issue_half = [&](int tn) {
+#pragma unroll
+            for (int j = 0; j < HALF; ++j)
+                if (tn + j < n) issue_tile<S, LAYOUT>(a, cx, tn + j, (tn + j) % STAGES);
+        };
         for (; t + S::GT <= n_full; t += S::GT) {
-            group_start(t);
             const char* gb = cx.smem + (t % STAGES) * S::STAGE;
+            // (the 17-24-block shape keeps the single burst: the split issue
+            // pushes its registers into spills)
+            if constexpr (S::R == 8 && S::NB >= 3) {
+                group_start(t);
+                tile(t, gb, Unmasked{}, std::integral_constant<int, 0>{});
+                if constexpr (S::GT >= 2) tile(t + 1, gb, Unmasked{}, std::integral_constant<int, S::STAGE>{});
+                if constexpr (S::GT >= 4) {
+                    tile(t + 2, gb, Unmasked{}, std::integral_constant<int, 2 * S::STAGE>{});
+                    tile(t + 3, gb, Unmasked{}, std::integral_constant<int, 3 * S::STAGE>{});
+                }
+                continue;
+            }
+            wait_vmcnt<0>();
+            barrier_lds();
+            issue_half(t + S::GT);
             tile(t, gb, Unmasked{}, std::integral_constant<int, 0>{});
-            if constexpr (S::GT >= 2) tile(t + 1, gb, Unmasked{}, std::integral_constant<int, S::STAGE>{});
-            if constexpr (S::GT >= 4) {
+            if constexpr (S::GT == 2) {
+                issue_half(t + S::GT + HALF);
+                tile(t + 1, gb, Unmasked{}, std::integral_constant<int, S::STAGE>{});
+            }
+            if constexpr (S::GT == 4) {
+                tile(t + 1, gb, Unmasked{}, std::integral_constant<int, S::STAGE>{});
+                issue_half(t + S::GT + HALF);
                 tile(t + 2, gb, Unmasked{}, std::integral_constant<int, 2 * S::STAGE>{});
                 tile(t + 3, gb, Unmasked{}, std::integral_constant<int, 3 * S::STAGE>{});
             }
