@@ -151,7 +151,6 @@ int tsw_tree_attn_split(const tsw_attn_desc* desc, const void* q, const void* k,
 int tsw_lse_merge(int32_t n_splits, int64_t n_rows, int32_t d, const float* part_o,
                   const float* part_lse, float* o, float* lse, tsw_stream_t stream);
 
-/* Static description of a status code. */
 /* ---------------------------------------------------------------------
  * Paged batch: B sequences that share one tree shape (same T and parent[])
  * but each have their own committed length n_prefix[b] and their own queries,
@@ -321,6 +320,19 @@ int tsw_kv_compact(void* k, void* v, int32_t n_layers, int64_t layer_stride, int
                    int32_t dtype, int64_t kv_head_stride, int64_t n_prefix, int32_t T,
                    const int32_t* result, tsw_stream_t stream);
 
+/* ---------------------------------------------------------------------
+ * Measurement aid (not a step of the method): the read-stream ceiling of
+ * this device for the cache a tsw_tree_attn_verify call with this desc
+ * reads.  Streams rows 0 .. n_prefix + T - 1 of every kv head of k and v
+ * through the same kind of LDS-DMA ring and grid as the matrix-core split
+ * kernel, with no arithmetic, so its rate (2 * Hkv * (n_prefix + T) * d * 2
+ * bytes per call) bounds what the split kernel can stream.  bfloat16,
+ * d = 128; k and v 16-byte aligned; sink: device memory of at least 64 bytes
+ * (never written for real data).  Errors: TSW_EINVAL, TSW_EUNSUPPORTED,
+ * TSW_EHIP. */
+int tsw_read_stream(const tsw_attn_desc* desc, const void* k, const void* v, unsigned* sink, tsw_stream_t stream);
+
+/* Static description of a status code. */
 const char* tsw_status_str(int status);
 
 #ifdef __cplusplus

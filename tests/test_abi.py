@@ -318,3 +318,16 @@ def test_accept_penalized_argument_errors(L):
     assert call(recent=None) == EINVAL
     assert call(n_recent=-2) == EINVAL
     assert call(ws=None) == EINVAL
+
+
+def test_read_stream_argument_errors(L):
+    d = _desc()
+    assert L.tsw_read_stream(ctypes.byref(d), None, FAKE, FAKE, None) == EINVAL
+    assert L.tsw_read_stream(ctypes.byref(d), FAKE, FAKE, None, None) == EINVAL
+    d32 = _desc(dtype=tsw.DTYPE_F32)
+    assert L.tsw_read_stream(ctypes.byref(d32), FAKE, FAKE, FAKE, None) == EUNSUP
+    d64 = _desc(d=64, kv_head_stride=(100 + 13) * 64)
+    assert L.tsw_read_stream(ctypes.byref(d64), FAKE, FAKE, FAKE, None) == EUNSUP
+    odd = ctypes.c_void_p(0x10008)
+    assert L.tsw_read_stream(ctypes.byref(d), odd, FAKE, FAKE, None) == EINVAL
+

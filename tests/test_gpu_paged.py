@@ -122,29 +122,24 @@ def test_paged_matches_contiguous_call():
     assert float((o[0] - o2).abs().max()) <= TOL and float((lse[0] - l2).abs().max()) <= TOL
 
 
-def test_paged_bench_workload_sampled():
+def test_paged_bench_workload_all_rows():
     """The paged bench workload at its full size and in its launch
     configuration (eight GQA-8B sequences of 25600 ... 4800 committed tokens,
-    16-row pages of a permuted pool): sampled (node, head) rows of every
-    sequence against the oracle, and every row finite."""
+    16-row pages of a permuted pool): every (node, head) row of every
+    sequence against the oracle."""
     w = wl.PAGED_WORKLOADS["paged_gqa8b_b8"]
     q, kp, vp, table_t = wl.make_paged_inputs(w, "cuda")
     parent = w.parent()
     o, lse = tsw.tree_attn_verify_paged(q, kp, vp, table_t, list(w.lengths), parent)
     torch.cuda.synchronize()
-    assert torch.isfinite(o).all() and torch.isfinite(lse).all()
     table = table_t.cpu().numpy()
-    T, Hq = w.n_nodes, w.Hq
-    rng = np.random.default_rng(11)
+    T = w.n_nodes
     for b, n in enumerate(w.lengths):
-        rows = np.array(sorted(set([0, Hq - 1, (T - 1) * Hq] + rng.choice(T * Hq, 12, replace=False).tolist())),
-                        dtype=np.int32)
         k = contiguous(kp, table[b], n + T, w.page_rows)
         v = contiguous(vp, table[b], n + T, w.page_rows)
         o_ref, l_ref = oracle.tree_attn(wl.oracle_view(q[b]), wl.oracle_view(k), wl.oracle_view(v), parent, n,
-                                        1 / np.sqrt(128), rows=rows, nthreads=NTHREADS)
-        ri = torch.as_tensor(rows, device=o.device).long()
-        eo = float(np.max(np.abs(o[b].reshape(-1, 128)[ri].cpu().double().numpy() - o_ref)))
-        el = float(np.max(np.abs(lse[b].reshape(-1)[ri].cpu().double().numpy() - l_ref)))
-        say("  bench workload seq %d n_prefix %d: max|dO| %.3g max|dLSE| %.3g" % (b, n, eo, el))
+                                        1 / np.sqrt(128), nthreads=NTHREADS)
+        eo = float(np.max(np.abs(o[b].cpu().double().numpy() - o_ref)))
+        el = float(np.max(np.abs(lse[b].cpu().double().numpy() - l_ref)))
+        say("  bench workload seq %d n_prefix %d: max|dO| %.3g max|dLSE| %.3g (all rows)" % (b, n, eo, el))
         assert eo <= TOL and el <= TOL, (b, n, eo, el)

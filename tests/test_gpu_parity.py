@@ -1,8 +1,8 @@
 """GPU parity: the HIP path (through the C ABI) against the float64 oracle on
 identical seeded inputs.  Tolerances: max-abs 1e-5 on O and LSE for float32
 inputs, 4e-3 for bfloat16 inputs with float32 accumulation; tree masks are
-compared bit-exactly.  Large workloads are checked on sampled (node, head)
-rows that the oracle computes one by one, plus properties on every row."""
+compared bit-exactly.  Every workload, the 100K-token ones included, is
+compared on every (node, head) row."""
 import os
 import sys
 
@@ -104,31 +104,19 @@ def test_workload_gqa8b_8k(impl):
     check(o, lse, o_ref, l_ref, TOL["bf16"], "gqa8b_8k %s" % impl)
 
 
-def _sample_rows(T, Hq, n, seed):
-    rng = np.random.default_rng(seed)
-    fixed = [t * Hq + 0 for t in range(T)] + [t * Hq + (Hq - 1) for t in (0, T - 1)]
-    extra = rng.choice(T * Hq, size=n, replace=False).tolist()
-    return np.array(sorted(set(fixed + extra)), dtype=np.int32)
-
-
 @pytest.mark.parametrize("name", ["gqa8b_100k", "mha7b_100k", "gqa14b_100k"])
-def test_workload_100k_sampled(name):
+def test_workload_100k_all_rows(name):
+    """The 100K-token workloads at full size in the launch configuration the
+    bench times: every (node, head) row of O and LSE against the oracle."""
     w = wl.WORKLOADS[name]
     q, k, v = wl.make_qkv(w, device="cuda")
     o, lse = tsw.tree_attn_verify(q, k, v, w.parent(), w.n_prefix)
     torch.cuda.synchronize()
-    rows = _sample_rows(w.n_nodes, w.Hq, 24, w.seed)
+    say("%s: %d rows x %d keys against the oracle (%d threads)" % (name, w.n_nodes * w.Hq, w.n_prefix + w.n_nodes,
+                                                                  NTHREADS))
     o_ref, l_ref = oracle.tree_attn(wl.oracle_view(q), wl.oracle_view(k), wl.oracle_view(v),
-                                    w.parent(), w.n_prefix, w.scale(), rows=rows,
-                                    nthreads=NTHREADS)
-    ri = torch.as_tensor(rows, device=o.device).long()
-    check(o.reshape(-1, w.d)[ri], lse.reshape(-1)[ri], o_ref, l_ref, TOL["bf16"], name)
-    # every row: finite, and O is a convex combination of the head's V rows,
-    # so each column lies within that column's range over the cache
-    assert torch.isfinite(o).all() and torch.isfinite(lse).all()
-    vmin = v.float().amin(dim=1).repeat_interleave(w.G, dim=0)   # [Hq, d]
-    vmax = v.float().amax(dim=1).repeat_interleave(w.G, dim=0)
-    assert bool((o >= vmin.unsqueeze(0) - 1e-4).all()) and bool((o <= vmax.unsqueeze(0) + 1e-4).all())
+                                    w.parent(), w.n_prefix, w.scale(), nthreads=NTHREADS)
+    check(o, lse, o_ref, l_ref, TOL["bf16"], name)
 
 
 def test_workload_partial32_layers():

@@ -78,13 +78,14 @@ def lib():
     L.tsw_accept_workspace_size.argtypes = [i32, i64, ctypes.POINTER(sz)]
     L.tsw_accept_greedy.argtypes = [vp, i32, vp, i64, i32, vp, vp, vp, sz, vp]
     L.tsw_kv_compact.argtypes = [vp, vp, i32, i64, i32, i32, i32, i64, i64, i32, vp, vp]
+    L.tsw_read_stream.argtypes = [D, vp, vp, vp, vp]
     L.tsw_status_str.argtypes = [ctypes.c_int]
     L.tsw_status_str.restype = ctypes.c_char_p
     for name in ("tsw_tree_mask_build", "tsw_plan_splits", "tsw_workspace_size",
                  "tsw_tree_attn_verify", "tsw_tree_attn_partial", "tsw_tree_attn_split",
                  "tsw_lse_merge", "tsw_accept_workspace_size", "tsw_accept_greedy",
                  "tsw_kv_compact", "tsw_paged_workspace_size", "tsw_tree_attn_verify_paged",
-                 "tsw_select_workspace_size", "tsw_select_partial"):
+                 "tsw_select_workspace_size", "tsw_select_partial", "tsw_read_stream"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L
@@ -615,3 +616,23 @@ def prepare_verify_select(q, k, v, parent, n_prefix, n_keep, n_idx, o, lse, idx,
     args, keep, _ = _verify_select_args(q, k, v, parent, n_prefix, n_keep, n_idx, o, lse, idx, importance,
                                         workspace, scale, impl, stream)
     return PreparedCall(lib().tsw_tree_attn_verify_select, args, "tsw_tree_attn_verify_select", keep)
+
+
+def read_stream(q, k, v, n_prefix, sink, scale=None, stream=None):
+    """Read-stream ceiling for the cache a verify call with these shapes reads
+    (a measurement aid): streams K and V rows 0 .. n_prefix + T - 1 through
+    the LDS-DMA ring.  sink: a device tensor of at least 64 bytes."""
+    _check_tensors(q, k, v)
+    desc = make_desc(q, k, n_prefix, scale)
+    st = ctypes.c_void_p(stream.cuda_stream) if stream is not None else _stream(q)
+    _check(lib().tsw_read_stream(ctypes.byref(desc), _dev_ptr(k), _dev_ptr(v), _dev_ptr(sink), st),
+           "tsw_read_stream")
+
+
+def prepare_read_stream(q, k, v, n_prefix, sink, scale=None, stream=None):
+    _check_tensors(q, k, v)
+    desc = make_desc(q, k, n_prefix, scale)
+    st = ctypes.c_void_p((stream or torch.cuda.current_stream(q.device)).cuda_stream)
+    args = (ctypes.byref(desc), _dev_ptr(k), _dev_ptr(v), _dev_ptr(sink), st)
+    return PreparedCall(lib().tsw_read_stream, args, "tsw_read_stream", keep=(desc,))
+

@@ -16,7 +16,8 @@ MFMA_SHAPES = [(4, 1, 1), (4, 1, 2), (4, 1, 3), (4, 1, 4), (4, 2, 3), (4, 2, 4),
                (4, 4, 5), (8, 2, 2), (8, 4, 2), (8, 4, 3), (8, 8, 2), (8, 8, 3)]
 # (source, extra flags, object name)
 UNITS = [(os.path.join(CSRC, n), [], n + ".o")
-         for n in ("tsw_api.cpp", "tsw_kernels.hip", "tsw_mfma.hip", "tsw_accept.hip", "tsw_select.hip")] + [
+         for n in ("tsw_api.cpp", "tsw_kernels.hip", "tsw_mfma.hip", "tsw_accept.hip", "tsw_select.hip",
+                   "tsw_stream.hip")] + [
     (os.path.join(CSRC, "tsw_mfma_inst.hip"), ["-DTSW_W=%d" % w, "-DTSW_R=%d" % r, "-DTSW_NB=%d" % nb],
      "tsw_mfma_%d_%d_%d.o" % (w, r, nb)) for w, r, nb in MFMA_SHAPES]
 SOURCES = sorted(set(u[0] for u in UNITS))

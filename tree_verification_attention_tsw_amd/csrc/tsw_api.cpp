@@ -748,6 +748,24 @@ int tsw_tree_attn_verify_select(const tsw_attn_desc* desc, const void* q, const 
     return hip_status(tsw::launch_select_passes(imp, desc->n_prefix, keep, n_out, idx, scratch, 1, st));
 }
 
+int tsw_read_stream(const tsw_attn_desc* desc, const void* k, const void* v, unsigned* sink, tsw_stream_t stream) {
+    int rc = check_desc(desc);
+    if (rc != TSW_OK) return rc;
+    if (!k || !v || !sink) return TSW_EINVAL;
+    if (desc->dtype != TSW_DTYPE_BF16 || desc->d != 128) return TSW_EUNSUPPORTED;
+    if (((uintptr_t)k | (uintptr_t)v) & 15) return TSW_EINVAL;
+    if (desc->kv_head_stride % 8) return TSW_EINVAL;
+    int cus = 0;
+    rc = device_cus(&cus);
+    if (rc != TSW_OK) return rc;
+    int32_t n_splits = 0;
+    rc = plan(desc, desc->n_prefix, false, cus, &n_splits);
+    if (rc != TSW_OK) return rc;
+    const int64_t rows = desc->n_prefix + desc->T;
+    return hip_status(tsw::launch_read_stream(k, v, desc->Hkv, desc->kv_head_stride * 2, rows, n_splits, sink,
+                                              (hipStream_t)stream));
+}
+
 const char* tsw_status_str(int status) {
     switch (status) {
         case TSW_OK: return "ok";

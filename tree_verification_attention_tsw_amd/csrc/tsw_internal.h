@@ -31,7 +31,7 @@ struct SplitArgs {
     int64_t chunk_keys;      // prefix keys per split, a multiple of the kernel's key tile
     int32_t T, Hq, Hkv, G, M, n_splits;
     float scale_log2;        // scale * log2(e): scores are exponentiated base 2
-    int32_t B;               // sequences (grid z); 1 unless paged
+    int32_t B;               // sequences; 1 unless paged (grid x then enumerates every sequence's splits)
     uint64_t mask[64];       // ancestor-or-self bits per node
     // paged batch: k/v point at page pools [n_pages][Hkv][page_rows][d];
     // sequence b's logical page j is table[b * table_stride + j]
@@ -157,6 +157,11 @@ hipError_t launch_select_passes(const float* imp, int64_t n_prefix, int64_t n_ke
 hipError_t launch_importance_from_scores(const float* root_s, int64_t stride, const float* lse, int Hq,
                                          int64_t n_prefix, float c, int64_t n_keep, float* imp, uint32_t* totals,
                                          int32_t* idx, hipStream_t stream);
+
+// Read-stream ceiling (measurement aid): rows [0, rows) of n_kv_heads heads
+// of K and V (256-byte rows, head_bytes apart) through the LDS-DMA ring.
+hipError_t launch_read_stream(const void* k, const void* v, int n_kv_heads, int64_t head_bytes, int64_t rows,
+                              int n_splits, unsigned* sink, hipStream_t stream);
 
 // Key tile of the vector-ALU kernel and its query rows per work-group.
 constexpr int kValuTile = 64;

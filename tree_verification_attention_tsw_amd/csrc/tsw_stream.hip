@@ -1,0 +1,76 @@
+// Read-stream ceiling of the LDS-DMA path (a measurement aid, not a step of
+// the method): streams every K and V row a tree-verification call reads,
+// through the same kind of ring the matrix-core split kernel uses (two
+// 128-key load groups of 64 KB per work-group, each issued in two 32 KB
+// halves, one work-group per (split, kv head)), with no arithmetic.  Its
+// rate is the HBM read rate the split kernel could reach if its compute
+// were free.
+#include "tsw_device.h"
+#include "tsw_internal.h"
+
+namespace tsw {
+namespace {
+
+constexpr int kStreamWaves = 8;
+constexpr int kStreamTile = 64;                      // keys per half group
+constexpr int kStreamTileBytes = 2 * kStreamTile * 256;   // K tile + V tile
+constexpr int kStreamLoads = kStreamTile / 2 / kStreamWaves;  // 1 KB loads per wave per tile
+
+// rows [c0, c1) of one kv head's K and V (256-byte rows), tile t into
+// stage st; rows past c1 re-read row c1 - 1
+__device__ __forceinline__ void stream_issue(const char* kh, const char* vh, int64_t c0, int64_t c1, int t, int st,
+                                             char* smem, int w, int lane) {
+    char* sbase = smem + st * kStreamTileBytes;
+#pragma unroll
+    for (int i = 0; i < kStreamLoads; ++i) {
+        const int u = w * kStreamLoads + i;
+        const bool isv = u >= kStreamTile / 4;
+        const int grp = isv ? u - kStreamTile / 4 : u;
+        int64_t row = c0 + (int64_t)t * kStreamTile + grp * 4 + (lane >> 4);
+        if (row >= c1) row = c1 - 1;
+        const char* src = (isv ? vh : kh) + row * 256 + 16 * (lane & 15);
+        char* dst = sbase + (isv ? kStreamTile * 256 : 0) + grp * 1024;
+        __builtin_amdgcn_global_load_lds((const void*)src, (__attribute__((address_space(3))) void*)dst, 16, 0,
+                                         kStreamAux);
+    }
+}
+
+__global__ __launch_bounds__(kStreamWaves * 64, 1) void read_stream(const char* k, const char* v, int64_t head_bytes,
+                                                                     int64_t rows, int64_t chunk, unsigned* sink) {
+    __shared__ __attribute__((aligned(1024))) char smem[4 * kStreamTileBytes];
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const char* kh = k + (int64_t)blockIdx.y * head_bytes;
+    const char* vh = v + (int64_t)blockIdx.y * head_bytes;
+    const int64_t c0 = (int64_t)blockIdx.x * chunk;
+    const int64_t c1 = c0 + chunk < rows ? c0 + chunk : rows;
+    if (c0 >= c1) return;                                  // uniform: an empty split
+    const int n = (int)((c1 - c0 + kStreamTile - 1) / kStreamTile);
+    // two groups of two tiles in the ring; a group's tiles are issued one
+    // per tile of the group before it
+    for (int t = 0; t < 2 && t < n; ++t) stream_issue(kh, vh, c0, c1, t, t, smem, w, lane);
+    unsigned acc = 0;
+    for (int t = 0; t < n; t += 2) {
+        wait_vmcnt<0>();
+        barrier_lds();
+        if (t + 2 < n) stream_issue(kh, vh, c0, c1, t + 2, (t + 2) % 4, smem, w, lane);
+        acc ^= *(volatile unsigned*)(smem + (t % 4) * kStreamTileBytes + threadIdx.x * 4);
+        if (t + 3 < n) stream_issue(kh, vh, c0, c1, t + 3, (t + 3) % 4, smem, w, lane);
+        if (t + 1 < n) acc ^= *(volatile unsigned*)(smem + ((t + 1) % 4) * kStreamTileBytes + threadIdx.x * 4);
+    }
+    wait_vmcnt<0>();
+    // never true for the caller's data in practice; keeps the reads alive
+    if (acc == 0x9e3779b9u) sink[threadIdx.x & 15] = acc;
+}
+
+}  // namespace
+
+hipError_t launch_read_stream(const void* k, const void* v, int n_kv_heads, int64_t head_bytes, int64_t rows,
+                              int n_splits, unsigned* sink, hipStream_t stream) {
+    const int64_t chunk = (rows + n_splits - 1) / n_splits;
+    hipLaunchKernelGGL(read_stream, dim3(n_splits, n_kv_heads), dim3(kStreamWaves * 64), 0, stream,
+                       (const char*)k, (const char*)v, head_bytes, rows, chunk, sink);
+    return hipGetLastError();
+}
+
+}  // namespace tsw
