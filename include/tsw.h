@@ -321,6 +321,23 @@ int tsw_kv_compact(void* k, void* v, int32_t n_layers, int64_t layer_stride, int
                    const int32_t* result, tsw_stream_t stream);
 
 /* ---------------------------------------------------------------------
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * call as tsw_tree_attn_verify, same arguments and results, without a
+ * workspace argument.  The split partials live in a device array of this
+ * library, tsw_noalloc_scratch_bytes() = 32 MiB per GPU, held until the
+ * process ends; the call makes no allocation of any kind.  A problem whose
+ * tsw_workspace_size() exceeds it returns TSW_ENOSPACE before launching
+ * anything.  Every call on one GPU uses that GPU's array: calls that can
+ * overlap on one GPU (different streams, different host threads) race on
+ * it and must be serialised by the caller; calls on one stream are
+ * ordered.  Errors as for tsw_tree_attn_verify.
+ * ------------------------------------------------------------------- */
+size_t tsw_noalloc_scratch_bytes(void);
+int tsw_tree_attn_verify_noalloc(const tsw_attn_desc* desc, const void* q, const void* k, const void* v,
+                                 const int32_t* parent, float* o, float* lse, tsw_stream_t stream);
+
+/* ---------------------------------------------------------------------
  * Measurement aid (not a step of the method): the read-stream ceiling of
  * this device for the cache a tsw_tree_attn_verify call with this desc
  * reads.  Streams rows 0 .. n_prefix + T - 1 of every kv head of k and v

@@ -18,5 +18,5 @@ from ._binding import (  # noqa: F401
     PagedDesc, make_paged_desc, paged_workspace_size, tree_attn_verify_paged, prepare_verify_paged,
     select_workspace_size, select_partial, prepare_select,
     verify_select_workspace_size, tree_attn_verify_select, prepare_verify_select,
-    read_stream, prepare_read_stream,
+    read_stream, prepare_read_stream, noalloc_scratch_bytes, tree_attn_verify_noalloc,
 )

@@ -79,13 +79,17 @@ def lib():
     L.tsw_accept_greedy.argtypes = [vp, i32, vp, i64, i32, vp, vp, vp, sz, vp]
     L.tsw_kv_compact.argtypes = [vp, vp, i32, i64, i32, i32, i32, i64, i64, i32, vp, vp]
     L.tsw_read_stream.argtypes = [D, vp, vp, vp, vp]
+    L.tsw_tree_attn_verify_noalloc.argtypes = [D, vp, vp, vp, vp, vp, vp, vp]
+    L.tsw_noalloc_scratch_bytes.argtypes = []
+    L.tsw_noalloc_scratch_bytes.restype = ctypes.c_size_t
     L.tsw_status_str.argtypes = [ctypes.c_int]
     L.tsw_status_str.restype = ctypes.c_char_p
     for name in ("tsw_tree_mask_build", "tsw_plan_splits", "tsw_workspace_size",
                  "tsw_tree_attn_verify", "tsw_tree_attn_partial", "tsw_tree_attn_split",
                  "tsw_lse_merge", "tsw_accept_workspace_size", "tsw_accept_greedy",
                  "tsw_kv_compact", "tsw_paged_workspace_size", "tsw_tree_attn_verify_paged",
-                 "tsw_select_workspace_size", "tsw_select_partial", "tsw_read_stream"):
+                 "tsw_select_workspace_size", "tsw_select_partial", "tsw_read_stream",
+                 "tsw_tree_attn_verify_noalloc"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L
@@ -636,3 +640,21 @@ def prepare_read_stream(q, k, v, n_prefix, sink, scale=None, stream=None):
     args = (ctypes.byref(desc), _dev_ptr(k), _dev_ptr(v), _dev_ptr(sink), st)
     return PreparedCall(lib().tsw_read_stream, args, "tsw_read_stream", keep=(desc,))
 
+
+
+def noalloc_scratch_bytes():
+    """Bytes of the library's own partials array used by tree_attn_verify_noalloc."""
+    return int(lib().tsw_noalloc_scratch_bytes())
+
+
+def tree_attn_verify_noalloc(q, k, v, parent, n_prefix, o, lse, scale=None, impl="auto", stream=None):
+    """tree_attn_verify without a workspace: the library's own device array
+    holds the split partials.  o [T, Hq, d] and lse [T, Hq] float32 are
+    written in place (the call allocates nothing)."""
+    _check_tensors(q, k, v)
+    desc = make_desc(q, k, n_prefix, scale, impl)
+    p = _parent_arr(parent)
+    st = ctypes.c_void_p(stream.cuda_stream) if stream is not None else _stream(q)
+    _check(lib().tsw_tree_attn_verify_noalloc(ctypes.byref(desc), _dev_ptr(q), _dev_ptr(k), _dev_ptr(v), _np_ptr(p),
+                                              _dev_ptr(o), _dev_ptr(lse), st), "tsw_tree_attn_verify_noalloc")
+    return o, lse

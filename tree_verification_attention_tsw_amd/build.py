@@ -17,7 +17,7 @@ MFMA_SHAPES = [(4, 1, 1), (4, 1, 2), (4, 1, 3), (4, 1, 4), (4, 2, 3), (4, 2, 4),
 # (source, extra flags, object name)
 UNITS = [(os.path.join(CSRC, n), [], n + ".o")
          for n in ("tsw_api.cpp", "tsw_kernels.hip", "tsw_mfma.hip", "tsw_accept.hip", "tsw_select.hip",
-                   "tsw_stream.hip")] + [
+                   "tsw_stream.hip", "tsw_noalloc.hip")] + [
     (os.path.join(CSRC, "tsw_mfma_inst.hip"), ["-DTSW_W=%d" % w, "-DTSW_R=%d" % r, "-DTSW_NB=%d" % nb],
      "tsw_mfma_%d_%d_%d.o" % (w, r, nb)) for w, r, nb in MFMA_SHAPES]
 SOURCES = sorted(set(u[0] for u in UNITS))
