@@ -15,15 +15,19 @@ The summaries record a digest of the split kernel's sources so that a
 reader (bench.py) can tell whether the counters still describe the current
 code.
 
-    python -m tree_verification_attention_tsw_amd.profiling stats DIR OUT --command "..."
+    python -m tree_verification_attention_tsw_amd.profiling stats DIR OUT --command "..." \\
+        [--window split_mfma FIRST COUNT] [--bench-log LOG]
     python -m tree_verification_attention_tsw_amd.profiling traffic FETCH_DIR WRITE_DIR OUT \\
         --kernel split_mfma --copy-mib 1024 --alg-bytes N --command "..." --command "..."
+    python -m tree_verification_attention_tsw_amd.profiling counters OUT DIR... --kernel NAME \\
+        --units-per-simd N --unit-name tile --command "..."
 """
 import argparse
 import collections
 import csv
 import glob
 import hashlib
+import json
 import os
 
 PKG = os.path.dirname(os.path.abspath(__file__))
@@ -113,13 +117,50 @@ def copy_factor(rows, counter, copy_bytes):
     return copy_bytes / (kib * 1024.0), kib
 
 
-def write_stats(d, out, commands):
+def trace_durations(d, kernel_substr):
+    """Durations (us) of the matching dispatches of a kernel trace, in start order."""
+    rows = [r for r in csv.DictReader(open(_find(d, "_kernel_trace.csv")))
+            if kernel_substr in r["Kernel_Name"]]
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    return [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in rows]
+
+
+def bench_line(path):
+    """The last JSON line a bench.py run printed."""
+    last = None
+    for line in open(path, errors="replace"):
+        if line.startswith("{"):
+            last = json.loads(line)
+    if last is None:
+        raise ValueError("no JSON line in %s" % path)
+    return last
+
+
+def write_stats(d, out, commands, window=None, bench_log=None):
+    """Whole-run kernel statistics; `window` = (kernel, first, count) adds the
+    mean over those dispatches of that kernel (the bench's timed steps), and
+    `bench_log` the bench line's own split time for comparison."""
     lines = ["# rocprofv3 kernel durations of the tsw kernels", "commands:"]
     lines += ["  " + c for c in commands]
     lines.append("source_digest: %s" % source_digest())
     lines.append("%-44s %6s %10s %10s %10s" % ("kernel", "calls", "avg_us", "min_us", "max_us"))
     for name, calls, avg, mn, mx in kernel_stats(d):
         lines.append("%-44s %6d %10.2f %10.2f %10.2f" % (name, calls, avg, mn, mx))
+    if window:
+        kernel, first, count = window
+        durs = trace_durations(d, kernel)[first:first + count]
+        if len(durs) != count:
+            raise ValueError("trace holds %d %s dispatches from %d, expected %d" % (len(durs), kernel, first, count))
+        srt = sorted(durs)
+        lines.append("timed steps (dispatches %d..%d of %s in start order): avg_us %.2f  median_us %.2f  "
+                     "min_us %.2f  max_us %.2f" % (first, first + count - 1, kernel, sum(durs) / count,
+                                                   srt[count // 2], srt[0], srt[-1]))
+    if bench_log:
+        b = bench_line(bench_log)
+        keys = ("ms_per_step", "us_per_layer_call", "us_split", "us_split_median5")
+        lines.append("bench line of the same run: " + ", ".join(
+            "%s %s" % (k, b[k]) for k in keys if b.get(k) is not None)
+            + (", roofline.us_per_launch %s" % b["roofline"]["us_per_launch"] if "roofline" in b else ""))
     _write(out, lines)
 
 
@@ -146,6 +187,67 @@ def write_traffic(fetch_dir, write_dir, out, kernel, copy_mib, alg_bytes, comman
     if alg_bytes:
         lines.append("alg_bytes_per_launch: %d" % alg_bytes)
         lines.append("traffic_over_alg: %.4f" % ((fb + wb) / alg_bytes))
+    _write(out, lines)
+
+
+def dispatch_durations(rows, kernel_substr):
+    """Per-dispatch duration (us) of the matching dispatches of a counter run."""
+    d = collections.OrderedDict()
+    for r in rows:
+        if kernel_substr in r["Kernel_Name"]:
+            d[int(r["Dispatch_Id"])] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+    return list(d.values())
+
+
+def write_counters(dirs, out, kernel, simds, xcds, units_per_simd, unit_name, commands):
+    """Average per-dispatch SQ/GRBM counters of `kernel` over several
+    rocprofv3 --pmc runs, with the derived per-SIMD quantities."""
+    vals = collections.OrderedDict()
+    durs = []
+    for d in dirs:
+        rows = counter_rows(d)
+        durs += dispatch_durations(rows, kernel)
+        names = sorted(set(r["Counter_Name"] for r in rows))
+        for c in names:
+            v = per_dispatch(rows, c, kernel)
+            if v:
+                vals[c] = sum(v) / len(v)
+    if not vals:
+        raise ValueError("no %s dispatches in the counter runs" % kernel)
+    dur = sum(durs) / len(durs)
+    lines = ["# SQ / GRBM counters per dispatch of %s (rocprofv3 --pmc, kernels serialised)" % kernel, "commands:"]
+    lines += ["  " + c for c in commands]
+    lines.append("source_digest: %s" % source_digest())
+    lines.append("dispatches: %d, mean duration under counter collection: %.2f us" % (len(durs), dur))
+    lines.append("raw counters (mean per dispatch, summed over the device as rocprofv3 reports them):")
+    for c, v in vals.items():
+        lines.append("  %-32s %18.1f" % (c, v))
+    lines.append("derived (%d SIMDs, %d XCDs, %g %s per SIMD):" % (simds, xcds, units_per_simd, unit_name))
+    clk = None
+    if "GRBM_GUI_ACTIVE" in vals:
+        cyc = vals["GRBM_GUI_ACTIVE"] / xcds
+        clk = cyc / (dur * 1e3)
+        lines.append("  clock: GRBM_GUI_ACTIVE / XCDs / duration = %.0f cycles / %.2f us = %.2f GHz" % (cyc, dur, clk))
+    if "SQ_VALU_MFMA_BUSY_CYCLES" in vals:
+        busy = vals["SQ_VALU_MFMA_BUSY_CYCLES"] / simds
+        lines.append("  MFMA busy cycles per SIMD: %.0f%s" % (
+            busy, " = %.1f%% of the kernel's cycles" % (100.0 * busy / (clk * dur * 1e3)) if clk else ""))
+    if "SQ_VALU_MFMA_COEXEC_CYCLES" in vals:
+        lines.append("  cycles with an MFMA busy and a VALU instruction issued, per SIMD: %.0f"
+                     % (vals["SQ_VALU_MFMA_COEXEC_CYCLES"] / simds))
+    for c, label in (("SQ_INSTS_MFMA", "MFMA instructions"), ("SQ_INSTS_VALU", "VALU instructions (MFMA included)"),
+                     ("SQ_INSTS_VALU_TRANS_F32", "transcendental (exp) instructions"),
+                     ("SQ_INSTS_LDS", "LDS instructions"), ("SQ_INSTS_SALU", "SALU instructions")):
+        if c in vals:
+            lines.append("  %s per SIMD per %s: %.1f" % (label, unit_name, vals[c] / simds / units_per_simd))
+    if "SQ_ACTIVE_INST_VALU" in vals:
+        lines.append("  VALU-active cycles per SIMD (SQ_ACTIVE_INST_VALU x 4 / SIMDs): %.0f"
+                     % (vals["SQ_ACTIVE_INST_VALU"] * 4 / simds))
+    if "SQ_WAIT_INST_ANY" in vals and "SQ_WAVES" in vals:
+        lines.append("  wave-cycles waiting to issue, per wave (SQ_WAIT_INST_ANY x 4 / waves): %.0f"
+                     % (vals["SQ_WAIT_INST_ANY"] * 4 / vals["SQ_WAVES"]))
+    if "SQ_LDS_BANK_CONFLICT" in vals:
+        lines.append("  LDS bank-conflict cycles per CU: %.0f" % (vals["SQ_LDS_BANK_CONFLICT"] / (simds / 4)))
     _write(out, lines)
 
 
@@ -176,6 +278,9 @@ def main():
     s.add_argument("dir")
     s.add_argument("out")
     s.add_argument("--command", action="append", default=[])
+    s.add_argument("--window", nargs=3, metavar=("KERNEL", "FIRST", "COUNT"),
+                   help="also report the mean over dispatches FIRST..FIRST+COUNT-1 of KERNEL")
+    s.add_argument("--bench-log", help="bench.py output of the profiled run")
     t = sub.add_parser("traffic")
     t.add_argument("fetch_dir")
     t.add_argument("write_dir")
@@ -184,9 +289,21 @@ def main():
     t.add_argument("--copy-mib", type=int, required=True)
     t.add_argument("--alg-bytes", type=int, default=0)
     t.add_argument("--command", action="append", default=[])
+    c = sub.add_parser("counters")
+    c.add_argument("out")
+    c.add_argument("dirs", nargs="+")
+    c.add_argument("--kernel", default="split_mfma")
+    c.add_argument("--simds", type=int, default=1024)
+    c.add_argument("--xcds", type=int, default=8)
+    c.add_argument("--units-per-simd", type=float, default=1.0)
+    c.add_argument("--unit-name", default="launch")
+    c.add_argument("--command", action="append", default=[])
     a = ap.parse_args()
     if a.cmd == "stats":
-        write_stats(a.dir, a.out, a.command)
+        win = (a.window[0], int(a.window[1]), int(a.window[2])) if a.window else None
+        write_stats(a.dir, a.out, a.command, win, a.bench_log)
+    elif a.cmd == "counters":
+        write_counters(a.dirs, a.out, a.kernel, a.simds, a.xcds, a.units_per_simd, a.unit_name, a.command)
     else:
         write_traffic(a.fetch_dir, a.write_dir, a.out, a.kernel, a.copy_mib, a.alg_bytes, a.command)
 
