@@ -191,6 +191,33 @@ int tsw_tree_attn_verify_paged(const tsw_paged_desc* desc, const void* q, const 
                                const int64_t* n_prefix, const int32_t* parent, float* o, float* lse,
                                void* workspace, size_t workspace_bytes, tsw_stream_t stream);
 
+/* Paged draft pass.  The draft model is the target model reading a partial
+ * KV cache ("90分钟生成10万Token…" (Tencent Cloud), 优势与特点 / 无损的输出质量;
+ * "TokenSwift - A framework…" (aiboss88), technical principles, dynamic KV
+ * cache update); over a batch of sequences in one page pool, each sequence's
+ * result is exactly tsw_tree_attn_partial's on that sequence's cache with its
+ * own index list:
+ *   idx   [B][idx_stride] int32   device; sequence b's list is
+ *         idx[b*idx_stride .. b*idx_stride + n_idx[b]), sorted ascending,
+ *         distinct, every entry in [0, n_prefix[b]) (a precondition, read on
+ *         the device); idx may be NULL when every n_idx[b] is 0
+ *   n_idx [B] int64               HOST; 0 <= n_idx[b] <= n_prefix[b]
+ *                                 (n_idx[b] = 0: the tree rows only)
+ *   idx_stride                    >= max n_idx[b]
+ * Tree node j still reads position n_prefix[b] + j through the block table.
+ * The pool must hold fewer than 2^32 rows per kv head (pages x page_rows);
+ * q, the pools, block_table, parent, o, lse and the workspace are as for
+ * tsw_tree_attn_verify_paged.  Errors: as that call, plus TSW_EBADINDEX (an
+ * n_idx[b] out of range) and TSW_EINVAL (idx_stride too small, idx NULL with
+ * a non-empty list). */
+int tsw_paged_partial_workspace_size(const tsw_paged_desc* desc, const int64_t* n_prefix,
+                                     const int64_t* n_idx, size_t* bytes);
+int tsw_tree_attn_partial_paged(const tsw_paged_desc* desc, const void* q, const void* k_pages,
+                                const void* v_pages, const int32_t* block_table,
+                                const int64_t* n_prefix, const int32_t* parent, const int32_t* idx,
+                                int64_t idx_stride, const int64_t* n_idx, float* o, float* lse,
+                                void* workspace, size_t workspace_bytes, tsw_stream_t stream);
+
 /* ---------------------------------------------------------------------
  * Partial-cache selection for the next draft pass.  The draft pass keeps the
  * initial positions and the most important others ("TokenSwift - A framework

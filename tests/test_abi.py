@@ -238,6 +238,37 @@ def test_paged_argument_errors(L):
     assert L.tsw_paged_workspace_size(ctypes.byref(_pdesc(B=0)), None, ctypes.byref(n)) == EINVAL
 
 
+def _ppaged(L, desc, npf=(100, 200, 0), nif=(50, 200, 0), idx=FAKE, stride=256, q=FAKE, ws=FAKE):
+    n = np.ascontiguousarray(np.asarray(npf, dtype=np.int64))
+    ni = np.ascontiguousarray(np.asarray(nif, dtype=np.int64)) if nif is not None else None
+    return L.tsw_tree_attn_partial_paged(ctypes.byref(desc), q, FAKE, FAKE, FAKE,
+                                         n.ctypes.data_as(ctypes.c_void_p),
+                                         PARENT.ctypes.data_as(ctypes.c_void_p), idx, stride,
+                                         ni.ctypes.data_as(ctypes.c_void_p) if ni is not None else None,
+                                         FAKE, FAKE, ws, 1 << 30, None)
+
+
+def test_paged_partial_argument_errors(L):
+    """The paged draft pass rejects bad index-list lengths and pointers
+    before any HIP call (as the verify call does its shape errors)."""
+    assert _ppaged(L, _pdesc(), nif=None) == EINVAL                      # no n_idx
+    assert _ppaged(L, _pdesc(), nif=(50, 201, 0)) == EBADINDEX           # n_idx > n_prefix
+    assert _ppaged(L, _pdesc(), nif=(-1, 0, 0)) == EBADINDEX
+    assert _ppaged(L, _pdesc(), stride=199) == EINVAL                    # a list longer than its row
+    assert _ppaged(L, _pdesc(), idx=None) == EINVAL                      # lists but no idx
+    assert _ppaged(L, _pdesc(), q=None) == EINVAL
+    assert _ppaged(L, _pdesc(B=0)) == EINVAL
+    assert _ppaged(L, _pdesc(d=64)) == EUNSUP
+    assert _ppaged(L, _pdesc(), npf=(100, -1, 0)) == EINVAL
+    n = ctypes.c_size_t(0)
+    npf = np.asarray([100, 200, 0], dtype=np.int64)
+    bad = np.asarray([0, 300, 0], dtype=np.int64)
+    assert L.tsw_paged_partial_workspace_size(ctypes.byref(_pdesc()), npf.ctypes.data_as(ctypes.c_void_p),
+                                              bad.ctypes.data_as(ctypes.c_void_p), ctypes.byref(n)) == EBADINDEX
+    assert L.tsw_paged_partial_workspace_size(ctypes.byref(_pdesc()), npf.ctypes.data_as(ctypes.c_void_p),
+                                              None, ctypes.byref(n)) == EINVAL
+
+
 def test_select_argument_errors(L):
     def call(desc=None, q=FAKE, k=FAKE, lse=FAKE, n_keep=128, n_idx=4096, idx=FAKE, imp=None, ws=FAKE):
         d = desc if desc is not None else _desc()

@@ -143,3 +143,105 @@ def test_paged_bench_workload_all_rows():
         el = float(np.max(np.abs(lse[b].cpu().double().numpy() - l_ref)))
         say("  bench workload seq %d n_prefix %d: max|dO| %.3g max|dLSE| %.3g (all rows)" % (b, n, eo, el))
         assert eo <= TOL and el <= TOL, (b, n, eo, el)
+
+
+# ------------------------------------------------------------ paged draft pass
+
+def index_lists(lengths, n_idx, seed, pad=3):
+    """Per-sequence sorted index lists (the first 64 positions kept) in the
+    rows of one int32 tensor with a few unused entries per row."""
+    stride = max(max(n_idx), 1) + pad
+    out = np.full((len(lengths), stride), -1, dtype=np.int32)
+    for b, (n, k) in enumerate(zip(lengths, n_idx)):
+        out[b, :k] = wl.retained_index_set(n, k, 64, seed * 100 + b)
+    return out
+
+
+def check_partial_batch(lengths, n_idx, T, Hq, Hkv, page_rows, seed, parent=None, no_lists=False):
+    parent = parent if parent is not None else wl.kary_tree_parent(T, 3)
+    q, kp, vp, table_t, table = make_batch(lengths, T, Hq, Hkv, page_rows, seed)
+    lists = index_lists(lengths, n_idx, seed)
+    say("paged draft pass B=%d T=%d Hq=%d Hkv=%d page=%d lengths=%s n_idx=%s" %
+        (len(lengths), T, Hq, Hkv, page_rows, lengths, n_idx))
+    idx_t = None if no_lists else torch.from_numpy(lists).cuda()
+    o, lse = tsw.tree_attn_partial_paged(q, kp, vp, table_t, lengths, parent, idx_t, n_idx)
+    torch.cuda.synchronize()
+    for b, (n, k) in enumerate(zip(lengths, n_idx)):
+        kc = contiguous(kp, table[b], n + T, page_rows)
+        vc = contiguous(vp, table[b], n + T, page_rows)
+        o_ref, l_ref = oracle.tree_attn(wl.oracle_view(q[b]), wl.oracle_view(kc), wl.oracle_view(vc), parent, n,
+                                        1 / np.sqrt(128), idx=lists[b, :k], nthreads=NTHREADS)
+        eo = float(np.max(np.abs(o[b].cpu().double().numpy() - o_ref)))
+        el = float(np.max(np.abs(lse[b].cpu().double().numpy() - l_ref)))
+        say("  seq %d n_prefix %d n_idx %d: max|dO| %.3g max|dLSE| %.3g" % (b, n, k, eo, el))
+        assert eo <= TOL and el <= TOL, (b, n, k, eo, el)
+
+
+def test_paged_partial_mixed_lengths():
+    # a whole cache as the list, an empty list, a list past one split's
+    # 4096-entry slice, tree rows crossing a page
+    check_partial_batch([4096, 3001, 777, 12000, 300], [1000, 3001, 0, 9000, 300], 40, 32, 8, 16, 11)
+
+
+def test_paged_partial_large_pages_and_mha():
+    check_partial_batch([2500, 6400], [2000, 5000], 13, 16, 16, 256, 12)
+
+
+def test_paged_partial_all_lists_empty():
+    """n_idx = 0 for every sequence, no index tensor: the tree rows only."""
+    check_partial_batch([1000, 2000, 50], [0, 0, 0], 13, 8, 2, 32, 13, no_lists=True)
+
+
+def test_paged_partial_draft_chain_many_sequences():
+    lengths = [600 + 311 * b for b in range(16)]
+    check_partial_batch(lengths, [min(n, 256 + 97 * b) for b, n in enumerate(lengths)], 4, 32, 8, 16, 14,
+                        parent=wl.chain_parent(4))
+
+
+def test_paged_partial_random_tree_T64():
+    check_partial_batch([2000, 4500], [1500, 4500], 64, 8, 2, 32, 15, parent=wl.random_tree_parent(64, 15))
+
+
+def test_paged_partial_gqa14b_shape():
+    check_partial_batch([3333, 9000], [3000, 4096], 40, 40, 8, 64, 16)
+
+
+def test_paged_partial_matches_contiguous_call():
+    """One sequence in pages vs the same cache and list contiguous: same
+    definition, two kernels; both within the tolerance of each other."""
+    T, Hq, Hkv, n, k = 4, 32, 8, 20000, 4096
+    parent = wl.chain_parent(T)
+    q, kp, vp, table_t, table = make_batch([n], T, Hq, Hkv, 16, 17)
+    lists = index_lists([n], [k], 17)
+    o, lse = tsw.tree_attn_partial_paged(q, kp, vp, table_t, [n], parent, torch.from_numpy(lists).cuda(), [k])
+    kc = contiguous(kp, table[0], n + T, 16)
+    vc = contiguous(vp, table[0], n + T, 16)
+    idx = torch.from_numpy(lists[0, :k].copy()).cuda()
+    o2, l2 = tsw.tree_attn_partial(q[0].contiguous(), kc, vc, parent, idx, n)
+    torch.cuda.synchronize()
+    assert float((o[0] - o2).abs().max()) <= TOL and float((lse[0] - l2).abs().max()) <= TOL
+
+
+def test_paged_partial_bench_workload_all_rows():
+    """The paged draft-pass bench workload at its full size and in its launch
+    configuration (eight GQA-8B sequences of 25600 ... 4800 committed tokens,
+    4096-position lists, four chained nodes, 16-row pages of a permuted
+    pool): every (node, head) row of every sequence against the oracle."""
+    w = wl.PAGED_WORKLOADS["paged_partial_gqa8b_b8"]
+    q, kp, vp, table_t = wl.make_paged_inputs(w, "cuda")
+    lists_t = wl.make_paged_index_lists(w, "cuda")
+    parent = w.parent()
+    o, lse = tsw.tree_attn_partial_paged(q, kp, vp, table_t, list(w.lengths), parent, lists_t, w.index_lengths())
+    torch.cuda.synchronize()
+    table, lists = table_t.cpu().numpy(), lists_t.cpu().numpy()
+    T = w.n_nodes
+    for b, (n, k) in enumerate(zip(w.lengths, w.index_lengths())):
+        kc = contiguous(kp, table[b], n + T, w.page_rows)
+        vc = contiguous(vp, table[b], n + T, w.page_rows)
+        o_ref, l_ref = oracle.tree_attn(wl.oracle_view(q[b]), wl.oracle_view(kc), wl.oracle_view(vc), parent, n,
+                                        1 / np.sqrt(128), idx=lists[b, :k], nthreads=NTHREADS)
+        eo = float(np.max(np.abs(o[b].cpu().double().numpy() - o_ref)))
+        el = float(np.max(np.abs(lse[b].cpu().double().numpy() - l_ref)))
+        say("  draft bench workload seq %d n_prefix %d n_idx %d: max|dO| %.3g max|dLSE| %.3g (all rows)"
+            % (b, n, k, eo, el))
+        assert eo <= TOL and el <= TOL, (b, n, eo, el)

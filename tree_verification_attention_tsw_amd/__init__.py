@@ -16,6 +16,7 @@ from ._binding import (  # noqa: F401
     accept_workspace_size, accept_greedy, prepare_accept, kv_compact, prepare_compact,
     context_penalty, prepare_penalty, accept_greedy_penalized, prepare_accept_penalized,
     PagedDesc, make_paged_desc, paged_workspace_size, tree_attn_verify_paged, prepare_verify_paged,
+    paged_partial_workspace_size, tree_attn_partial_paged, prepare_partial_paged,
     select_workspace_size, select_partial, prepare_select,
     verify_select_workspace_size, tree_attn_verify_select, prepare_verify_select,
     read_stream, prepare_read_stream, noalloc_scratch_bytes, tree_attn_verify_noalloc,

@@ -68,6 +68,8 @@ def lib():
     PD = ctypes.POINTER(PagedDesc)
     L.tsw_paged_workspace_size.argtypes = [PD, vp, ctypes.POINTER(sz)]
     L.tsw_tree_attn_verify_paged.argtypes = [PD, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.tsw_paged_partial_workspace_size.argtypes = [PD, vp, vp, ctypes.POINTER(sz)]
+    L.tsw_tree_attn_partial_paged.argtypes = [PD, vp, vp, vp, vp, vp, vp, vp, i64, vp, vp, vp, vp, sz, vp]
     L.tsw_select_workspace_size.argtypes = [i64, ctypes.POINTER(sz)]
     L.tsw_select_partial.argtypes = [D, vp, vp, vp, i64, i64, vp, vp, vp, sz, vp]
     L.tsw_verify_select_workspace_size.argtypes = [D, ctypes.POINTER(sz)]
@@ -89,7 +91,8 @@ def lib():
                  "tsw_lse_merge", "tsw_accept_workspace_size", "tsw_accept_greedy",
                  "tsw_kv_compact", "tsw_paged_workspace_size", "tsw_tree_attn_verify_paged",
                  "tsw_select_workspace_size", "tsw_select_partial", "tsw_read_stream",
-                 "tsw_tree_attn_verify_noalloc"):
+                 "tsw_tree_attn_verify_noalloc", "tsw_paged_partial_workspace_size",
+                 "tsw_tree_attn_partial_paged"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L
@@ -532,6 +535,56 @@ def prepare_verify_paged(q, k_pages, v_pages, block_table, n_prefix, parent, o, 
     args, keep = _paged_args(q, k_pages, v_pages, block_table, n_prefix, parent, o, lse, workspace, scale,
                              stream)
     return PreparedCall(lib().tsw_tree_attn_verify_paged, args, "tsw_tree_attn_verify_paged", keep)
+
+
+def paged_partial_workspace_size(q, k_pages, block_table, n_prefix, n_idx, scale=None):
+    desc = make_paged_desc(q, k_pages, block_table, scale)
+    npf, nif = _paged_lengths(n_prefix), _paged_lengths(n_idx)
+    n = ctypes.c_size_t(0)
+    _check(lib().tsw_paged_partial_workspace_size(ctypes.byref(desc), _np_ptr(npf), _np_ptr(nif),
+                                                  ctypes.byref(n)), "tsw_paged_partial_workspace_size")
+    return n.value
+
+
+def _paged_partial_args(q, k_pages, v_pages, block_table, n_prefix, parent, idx, n_idx, o, lse, workspace, scale,
+                        stream):
+    """idx: int32 GPU tensor [B, idx_stride] (sequence b's list in row b), or
+    None when every n_idx[b] is 0."""
+    args, keep = _paged_args(q, k_pages, v_pages, block_table, n_prefix, parent, o, lse, workspace, scale, stream)
+    if idx is not None:
+        if idx.dtype != torch.int32 or not idx.is_cuda or not idx.is_contiguous() or idx.dim() != 2:
+            raise ValueError("idx must be a contiguous 2-D int32 GPU tensor [B, idx_stride]")
+        stride = idx.shape[1]
+    else:
+        stride = 0
+    nif = _paged_lengths(n_idx)
+    # (desc, q, k, v, table, n_prefix, parent, idx, idx_stride, n_idx, o, lse, ws, ws_bytes, stream)
+    args = args[:7] + (_dev_ptr(idx) if idx is not None else None, stride, _np_ptr(nif)) + args[7:]
+    return args, keep + (nif, idx)
+
+
+def tree_attn_partial_paged(q, k_pages, v_pages, block_table, n_prefix, parent, idx, n_idx, scale=None, out=None,
+                            workspace=None):
+    """Paged batch draft pass over per-sequence index lists; returns
+    (o [B, T, Hq, d], lse [B, T, Hq])."""
+    B, T, Hq, d = q.shape
+    o, lse = out if out is not None else (
+        torch.empty((B, T, Hq, d), dtype=torch.float32, device=q.device),
+        torch.empty((B, T, Hq), dtype=torch.float32, device=q.device))
+    if workspace is None:
+        workspace = torch.empty(max(paged_partial_workspace_size(q, k_pages, block_table, n_prefix, n_idx, scale),
+                                    256), dtype=torch.uint8, device=q.device)
+    args, _keep = _paged_partial_args(q, k_pages, v_pages, block_table, n_prefix, parent, idx, n_idx, o, lse,
+                                      workspace, scale, None)
+    _check(lib().tsw_tree_attn_partial_paged(*args), "tsw_tree_attn_partial_paged")
+    return o, lse
+
+
+def prepare_partial_paged(q, k_pages, v_pages, block_table, n_prefix, parent, idx, n_idx, o, lse, workspace,
+                          scale=None, stream=None):
+    args, keep = _paged_partial_args(q, k_pages, v_pages, block_table, n_prefix, parent, idx, n_idx, o, lse,
+                                     workspace, scale, stream)
+    return PreparedCall(lib().tsw_tree_attn_partial_paged, args, "tsw_tree_attn_partial_paged", keep)
 
 
 # ------------------------------------------------------------ partial-cache selection

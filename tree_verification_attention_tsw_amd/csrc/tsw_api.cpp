@@ -289,22 +289,23 @@ int check_paged(const tsw_paged_desc* d, const int64_t* n_prefix, int64_t* n_max
     return TSW_OK;
 }
 
-// Paged split plan: about one work-group per CU and kv head for the whole
-// batch, dealt so that the longest per-split slice (in key tiles) is as short
-// as possible; sequence b gets seg_base[b+1] - seg_base[b] splits (at least
-// one) of ceil(n_prefix[b] / splits) keys rounded up to whole tiles, and its
-// slices' pages must fit the LDS table.
-int plan_paged(const tsw_paged_desc* d, const int64_t* n_prefix, const tsw::MfmaConfig& cfg, int32_t* seg_base) {
+// Split plan of a batch: about one work-group per CU and kv head for the
+// whole batch, dealt so that the longest per-split slice (in key tiles) is as
+// short as possible; sequence b gets seg_base[b+1] - seg_base[b] splits (at
+// least one) of ceil(len[b] / splits) keys rounded up to whole tiles, and no
+// slice longer than max_tiles tiles (what the kernel stages in LDS).  len is
+// the committed length (verify) or the index-list length (draft pass).
+int plan_segments(const tsw_paged_desc* d, const int64_t* len, const tsw::MfmaConfig& cfg, int64_t max_tiles,
+                  int32_t* seg_base) {
     int cus = 0;
     int rc = device_cus(&cus);
     if (rc != TSW_OK) return rc;
     const int64_t tk = cfg.tile_keys();
     int64_t target = cus / d->Hkv;
     if (target < d->B) target = d->B;
-    const int64_t max_tiles = kPagedSlicePages * d->page_rows / tk;
     // splits sequence b needs so that none of its slices exceeds `tiles`
     auto splits_for = [&](int64_t b, int64_t tiles) {
-        const int64_t nt = cdiv(n_prefix[b], tk);
+        const int64_t nt = cdiv(len[b], tk);
         const int64_t sb = cdiv(nt, tiles);
         return sb < 1 ? (int64_t)1 : sb;
     };
@@ -315,7 +316,7 @@ int plan_paged(const tsw_paged_desc* d, const int64_t* n_prefix, const tsw::Mfma
     };
     // smallest per-split tile count whose split total fits the target
     int64_t lo = 2, hi = 2;
-    for (int b = 0; b < d->B; ++b) hi = cdiv(n_prefix[b], tk) > hi ? cdiv(n_prefix[b], tk) : hi;
+    for (int b = 0; b < d->B; ++b) hi = cdiv(len[b], tk) > hi ? cdiv(len[b], tk) : hi;
     while (lo < hi) {
         const int64_t mid = (lo + hi) / 2;
         if (total_for(mid) <= target) hi = mid;
@@ -328,6 +329,33 @@ int plan_paged(const tsw_paged_desc* d, const int64_t* n_prefix, const tsw::Mfma
         if (seg_base[b] + sb > 65535) return TSW_EUNSUPPORTED;
         seg_base[b + 1] = (int32_t)(seg_base[b] + sb);
     }
+    return TSW_OK;
+}
+
+// Verify: a split's pages must fit the LDS page table.
+int plan_paged(const tsw_paged_desc* d, const int64_t* n_prefix, const tsw::MfmaConfig& cfg, int32_t* seg_base) {
+    return plan_segments(d, n_prefix, cfg, kPagedSlicePages * d->page_rows / cfg.tile_keys(), seg_base);
+}
+
+// Draft pass: a split's index slice must fit the LDS index buffer.
+int plan_paged_partial(const tsw_paged_desc* d, const int64_t* n_idx, const tsw::MfmaConfig& cfg,
+                       int32_t* seg_base) {
+    return plan_segments(d, n_idx, cfg, tsw::kGatherChunkMax / cfg.tile_keys(), seg_base);
+}
+
+// Index lists of a paged draft pass: 0 <= n_idx[b] <= n_prefix[b], each
+// list within its row of idx_stride entries.
+int check_paged_idx(const tsw_paged_desc* d, const int64_t* n_prefix, const int32_t* idx, int64_t idx_stride,
+                    const int64_t* n_idx) {
+    if (!n_idx) return TSW_EINVAL;
+    int64_t most = 0;
+    for (int b = 0; b < d->B; ++b) {
+        if (n_idx[b] < 0 || n_idx[b] > n_prefix[b]) return TSW_EBADINDEX;
+        if (n_idx[b] > most) most = n_idx[b];
+    }
+    if (most > 0 && !idx) return TSW_EINVAL;
+    if (idx_stride < most) return TSW_EINVAL;
+    if (most > INT32_MAX) return TSW_EUNSUPPORTED;
     return TSW_OK;
 }
 
@@ -575,13 +603,41 @@ int tsw_paged_workspace_size(const tsw_paged_desc* desc, const int64_t* n_prefix
     return TSW_OK;
 }
 
-int tsw_tree_attn_verify_paged(const tsw_paged_desc* desc, const void* q, const void* k_pages, const void* v_pages,
-                               const int32_t* block_table, const int64_t* n_prefix, const int32_t* parent, float* o,
-                               float* lse, void* workspace, size_t workspace_bytes, tsw_stream_t stream) {
+int tsw_paged_partial_workspace_size(const tsw_paged_desc* desc, const int64_t* n_prefix, const int64_t* n_idx,
+                                     size_t* bytes) {
+    if (!bytes) return TSW_EINVAL;
     int64_t n_max = 0;
     tsw::MfmaConfig cfg;
     int rc = check_paged(desc, n_prefix, &n_max, &cfg);
     if (rc != TSW_OK) return rc;
+    if (!n_idx) return TSW_EINVAL;
+    for (int b = 0; b < desc->B; ++b)
+        if (n_idx[b] < 0 || n_idx[b] > n_prefix[b]) return TSW_EBADINDEX;
+    int32_t seg_base[65];
+    rc = plan_paged_partial(desc, n_idx, cfg, seg_base);
+    if (rc != TSW_OK) return rc;
+    *bytes = ws_bytes_paged(desc, seg_base[desc->B]);
+    return TSW_OK;
+}
+
+namespace {
+
+// Both paged calls: the split over every sequence's key list (its committed
+// positions, or its index list when idx_list is set), then the merge of each
+// sequence's parts.
+int paged_call(const tsw_paged_desc* desc, const void* q, const void* k_pages, const void* v_pages,
+               const int32_t* block_table, const int64_t* n_prefix, const int32_t* parent, const int32_t* idx_list,
+               int64_t idx_stride, const int64_t* n_idx, float* o, float* lse, void* workspace,
+               size_t workspace_bytes, tsw_stream_t stream) {
+    int64_t n_max = 0;
+    tsw::MfmaConfig cfg;
+    int rc = check_paged(desc, n_prefix, &n_max, &cfg);
+    if (rc != TSW_OK) return rc;
+    const bool gather = n_idx != nullptr;
+    if (gather) {
+        rc = check_paged_idx(desc, n_prefix, idx_list, idx_stride, n_idx);
+        if (rc != TSW_OK) return rc;
+    }
     if (!q || !k_pages || !v_pages || !block_table || !parent || !o || !lse || !workspace) return TSW_EINVAL;
     if (((uintptr_t)q | (uintptr_t)k_pages | (uintptr_t)v_pages) & 15) return TSW_EINVAL;
     if ((uintptr_t)workspace & 255) return TSW_EINVAL;
@@ -589,7 +645,7 @@ int tsw_tree_attn_verify_paged(const tsw_paged_desc* desc, const void* q, const 
     memset(&a, 0, sizeof a);
     rc = build_mask(parent, desc->T, a.mask, nullptr);
     if (rc != TSW_OK) return rc;
-    rc = plan_paged(desc, n_prefix, cfg, a.seg_base);
+    rc = gather ? plan_paged_partial(desc, n_idx, cfg, a.seg_base) : plan_paged(desc, n_prefix, cfg, a.seg_base);
     if (rc != TSW_OK) return rc;
     const int32_t n_splits = a.seg_base[desc->B];
     if (workspace_bytes < ws_bytes_paged(desc, n_splits)) return TSW_ENOSPACE;
@@ -618,7 +674,14 @@ int tsw_tree_attn_verify_paged(const tsw_paged_desc* desc, const void* q, const 
     a.page_shift = shift;
     a.page_bytes = (int64_t)desc->Hkv * desc->page_rows * desc->d * 2;
     for (int b = 0; b < desc->B; ++b) a.npb[b] = n_prefix[b];
-    rc = hip_status(tsw::launch_split_mfma(cfg, tsw::kModePaged, a, desc->Hkv, (hipStream_t)stream));
+    if (gather) {
+        for (int b = 0; b < desc->B; ++b) a.nib[b] = n_idx[b];
+        // an all-empty batch still passes a non-null list; no entry is read
+        a.idx = idx_list ? idx_list : (const int32_t*)workspace;
+        a.idx_stride = idx_stride;
+    }
+    rc = hip_status(tsw::launch_split_mfma(cfg, gather ? tsw::kModePagedGather : tsw::kModePaged, a, desc->Hkv,
+                                           (hipStream_t)stream));
     if (rc != TSW_OK) return rc;
     tsw::MergeSegs segs;
     memset(&segs, 0, sizeof segs);
@@ -627,6 +690,24 @@ int tsw_tree_attn_verify_paged(const tsw_paged_desc* desc, const void* q, const 
     for (int b = 0; b <= desc->B; ++b) segs.base[b] = a.seg_base[b];
     return hip_status(tsw::launch_lse_merge_segs(segs, (int64_t)rows_per_seq * desc->B, part_o, part_lse, o, lse,
                                                  (hipStream_t)stream));
+}
+
+}  // namespace
+
+int tsw_tree_attn_verify_paged(const tsw_paged_desc* desc, const void* q, const void* k_pages, const void* v_pages,
+                               const int32_t* block_table, const int64_t* n_prefix, const int32_t* parent, float* o,
+                               float* lse, void* workspace, size_t workspace_bytes, tsw_stream_t stream) {
+    return paged_call(desc, q, k_pages, v_pages, block_table, n_prefix, parent, nullptr, 0, nullptr, o, lse,
+                      workspace, workspace_bytes, stream);
+}
+
+int tsw_tree_attn_partial_paged(const tsw_paged_desc* desc, const void* q, const void* k_pages, const void* v_pages,
+                                const int32_t* block_table, const int64_t* n_prefix, const int32_t* parent,
+                                const int32_t* idx, int64_t idx_stride, const int64_t* n_idx, float* o, float* lse,
+                                void* workspace, size_t workspace_bytes, tsw_stream_t stream) {
+    if (!n_idx) return TSW_EINVAL;
+    return paged_call(desc, q, k_pages, v_pages, block_table, n_prefix, parent, idx, idx_stride, n_idx, o, lse,
+                      workspace, workspace_bytes, stream);
 }
 
 int tsw_select_workspace_size(int64_t n_prefix, size_t* bytes) {

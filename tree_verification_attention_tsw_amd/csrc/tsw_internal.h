@@ -9,11 +9,11 @@
 namespace tsw {
 
 // How the split kernels find a key's K/V row: the cache position itself
-// (contiguous), through an index list (gather, the draft pass), or through
-// a per-sequence block table into a page pool (paged batch).
-// Key layouts of the split kernel; kModeContigRoot is the contiguous layout
-// that also writes the root row's scores (SplitArgs::root_s).
-enum { kModeContig = 0, kModeGather = 1, kModePaged = 2, kModeContigRoot = 3 };
+// (contiguous), through an index list (gather, the draft pass), through a
+// per-sequence block table into a page pool (paged batch), or through both
+// (paged draft pass: index list -> position -> page).  kModeContigRoot is the
+// contiguous layout that also writes the root row's scores (SplitArgs::root_s).
+enum { kModeContig = 0, kModeGather = 1, kModePaged = 2, kModeContigRoot = 3, kModePagedGather = 4 };
 
 // Everything a split kernel needs, passed by value as the kernel argument.
 // The tree mask travels here (one 64-bit word per node) so that no device
@@ -23,6 +23,7 @@ struct SplitArgs {
     const void* k;           // [Hkv][rows][d], kv_head_stride elements per head
     const void* v;
     const int32_t* idx;      // partial variant: sorted prefix positions; nullptr for verify
+                             // (paged draft pass: sequence b's list at idx + b * idx_stride)
     float* part_o;           // [n_splits][T][Hq][d]
     float* part_lse;         // [n_splits][T][Hq], natural log
     int64_t n_prefix;        // the tree rows start at this cache position
@@ -39,6 +40,8 @@ struct SplitArgs {
     int32_t table_stride, page_rows, page_shift, pad_;
     int64_t page_bytes;      // Hkv * page_rows * d * 2: one page of the pool
     int64_t npb[64];         // committed length per sequence
+    int64_t nib[64];         // paged draft pass: index-list length per sequence
+    int64_t idx_stride;      // paged draft pass: entries between sequences' index lists
     // splits of sequence b are grid x in [seg_base[b], seg_base[b+1]), each
     // ceil(n / splits) keys rounded up to whole tiles, but the last
     int32_t seg_base[65];
@@ -49,6 +52,8 @@ struct SplitArgs {
     int64_t root_stride;     // a multiple of 4
     uint32_t* root_clear;    // kModeContigRoot: 1024 words zeroed by work-group (0, 0), or nullptr
 };
+// kernel arguments are limited to 4 KB
+static_assert(sizeof(SplitArgs) <= 4096, "SplitArgs must fit the kernel-argument segment");
 
 // Partial rows grouped by sequence for the merge: sequence s owns splits
 // [base[s], base[s+1]), each split holding rows_per_seg rows.  A single

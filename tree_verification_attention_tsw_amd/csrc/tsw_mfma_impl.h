@@ -68,7 +68,10 @@ struct Shape {
     // gather and paged variants the staged index or page-table slice.
     static constexpr int POOL = WAVES * 4;            // the work-group vote
     static constexpr int MASK_BYTES = 64 * 8;
-    static constexpr int IDX_BYTES = MODE_ != kModeContig ? kGatherChunkMax * 4 : 0;
+    // (paged draft pass: the slice's pool rows, then the tree rows' after it)
+    static constexpr int IDX_BYTES = MODE_ == kModeContig ? 0
+                                     : MODE_ == kModePagedGather ? (kGatherChunkMax + 64) * 4
+                                                                 : kGatherChunkMax * 4;
     static constexpr int RESERVE = ((POOL + MASK_BYTES + 255) & ~255) + IDX_BYTES;
     // Loads are issued, waited for and recycled in groups of GT tiles, 128
     // keys (32 KB of K and 32 KB of V) per group, with one barrier per group.
@@ -95,7 +98,8 @@ struct Shape {
 
 struct Ctx {
     char* smem;
-    const int32_t* idx_lds;      // gather: index slice; paged: page-table slices
+    const int32_t* idx_lds;      // gather: index slice; paged: page-table slices;
+                                 // paged gather: pool rows of the slice and the tree rows
     const uint64_t* mask_lds;    // the tree mask, copied to LDS
     const char* kbase;           // this kv head's cache (paged: the page pool)
     const char* vbase;
@@ -137,7 +141,34 @@ __device__ __forceinline__ void issue_tile(const SplitArgs& a, const Ctx& cx, in
         }
         return;
     }
-    if constexpr (MODE != kModePaged) {
+    if constexpr (MODE == kModePagedGather) {
+        // paged draft pass: the staged entries are pool rows (page number
+        // times page_rows plus the row in the page), prefix slice first and
+        // the tree rows at kGatherChunkMax
+#pragma unroll
+        for (int i = 0; i < S::NI; ++i) {
+            const int u = cx.w * S::NI + i;
+            const bool isv = u >= S::TK / 4;
+            const int grp = isv ? u - S::TK / 4 : u;
+            const int row = grp * 4 + cx.lj;
+            int slot;
+            if (pre) {
+                int64_t kk = k0 + row;
+                if (kk >= cx.c1) kk = cx.c0;
+                slot = (int)(kk - cx.c0);
+            } else {
+                int jj = (tt - cx.n_pre_tiles) * S::TK + row;
+                if (jj >= a.T) jj = a.T - 1;
+                slot = kGatherChunkMax + jj;
+            }
+            const uint32_t prow = (uint32_t)cx.idx_lds[slot];
+            const char* src = (isv ? cx.vbase : cx.kbase) + (uint64_t)(prow >> a.page_shift) * (uint64_t)a.page_bytes +
+                              (uint32_t)((prow & (uint32_t)(a.page_rows - 1)) * S::ROWB + 16 * (cx.li ^ swz(row)));
+            char* dst = sbase + (isv ? S::TK * S::ROWB : 0) + grp * 1024;
+            __builtin_amdgcn_global_load_lds((const void*)src, (__attribute__((address_space(3))) void*)dst, 16, 0,
+                                             kStreamAux);
+        }
+    } else if constexpr (MODE != kModePaged) {
 #pragma unroll
         for (int i = 0; i < S::NI; ++i) {
             const int u = cx.w * S::NI + i;
@@ -276,9 +307,14 @@ __device__ __forceinline__ void qk_block(const bf16x8 (&kop)[2][4], const bf16x8
 
 // p = 2^(s*c - mu) for one block, rounded to bf16 for the P V product; the
 // row sum adds the same rounded values (v_dot2c_f32_bf16 with (1, 1)), so
-// the normalisation matches the weights actually applied to V.
-template <bool SHIFT>
-__device__ __forceinline__ void softmax_block(const f32x4 (&sc)[2], float c, float mu, float& l, bf16x8& pb) {
+// the normalisation matches the weights actually applied to V.  With SPLIT
+// (masked tiles: the ragged end of a slice and the tree's own rows, where a
+// row may see only a handful of keys and single rounding errors do not
+// average out) p is carried as bf16 pb + bf16 pl, pl the rounding residue,
+// about 16 significant bits; both go through P V and into the row sum.
+template <bool SHIFT, bool SPLIT = false>
+__device__ __forceinline__ void softmax_block(const f32x4 (&sc)[2], float c, float mu, float& l, bf16x8& pb,
+                                              bf16x8& pl) {
     const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
@@ -286,11 +322,25 @@ __device__ __forceinline__ void softmax_block(const f32x4 (&sc)[2], float c, flo
         for (int i = 0; i < 4; i += 2) {
             const float t0 = SHIFT ? fmaf(sc[kb][i], c, -mu) : sc[kb][i] * c;
             const float t1 = SHIFT ? fmaf(sc[kb][i + 1], c, -mu) : sc[kb][i + 1] * c;
-            const bf16x2 pp = {(__bf16)exp2_fast(t0), (__bf16)exp2_fast(t1)};
+            const float e0 = exp2_fast(t0), e1 = exp2_fast(t1);
+            const bf16x2 pp = {(__bf16)e0, (__bf16)e1};
             l = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, l, false);
             pb[kb * 4 + i] = pp[0];
             pb[kb * 4 + i + 1] = pp[1];
+            if constexpr (SPLIT) {
+                // e - hi is exact in float; -inf scores give e = 0, hi = 0
+                const bf16x2 rr = {(__bf16)(e0 - (float)pp[0]), (__bf16)(e1 - (float)pp[1])};
+                l = __builtin_amdgcn_fdot2_f32_bf16(rr, ones, l, false);
+                pl[kb * 4 + i] = rr[0];
+                pl[kb * 4 + i + 1] = rr[1];
+            }
         }
+}
+
+template <bool SHIFT>
+__device__ __forceinline__ void softmax_block(const f32x4 (&sc)[2], float c, float mu, float& l, bf16x8& pb) {
+    bf16x8 unused;
+    softmax_block<SHIFT, false>(sc, c, mu, l, pb, unused);
 }
 
 __device__ __forceinline__ void pv_block(const bf16x8& pb, const bf16x8 (&vop)[8], f32x4 (&ob)[8]) {
@@ -339,10 +389,11 @@ __device__ __forceinline__ void tile_pv(const SplitArgs& a, const Ctx& cx, int t
         }
         if constexpr (EMIT)
             if (b == 0) emit_root<S, MASKED>(a, cx, tt, sc[0]);
-        bf16x8 pb;
+        bf16x8 pb, pl;
         // a wave whose key sub-tiles held no visible key for a row has m = -inf
-        softmax_block<SHIFT>(sc[b & 1], c, (SHIFT && m[b] != -INFINITY) ? m[b] : 0.0f, l[b], pb);
+        softmax_block<SHIFT, MASKED>(sc[b & 1], c, (SHIFT && m[b] != -INFINITY) ? m[b] : 0.0f, l[b], pb, pl);
         pv_block(pb, vop, o[b]);
+        if constexpr (MASKED) pv_block(pl, vop, o[b]);
     }
 }
 
@@ -355,6 +406,11 @@ template <class S, int NBA, bool MASKED, bool SHIFT, bool EMIT, int SOFF = 0>
 __device__ __forceinline__ void tile_pv_shared(const SplitArgs& a, const Ctx& cx, int tt, float c, const char* Ks,
                                                const bf16x8 (&qop)[NBA][4], const float (&m)[NBA],
                                                float (&l)[NBA], f32x4 (&o)[NBA][8]) {
+    constexpr int VOFF = SOFF + S::TK * S::ROWB;
+    const int trow0 = cx.ks * 32 + 4 * cx.lj + (cx.li >> 2);
+    const int tsel = (cx.li >> 1) & 1;
+    const char* vrow0 = Ks + trow0 * S::ROWB + 8 * (cx.li & 1);
+    const int sw0 = swz(trow0) ^ tsel;
     f32x4 sc[NBA][2];
 #pragma unroll
     for (int b = 0; b < NBA; ++b) s_init<S, MASKED>(a, cx, tt, b, sc[b]);
@@ -372,14 +428,9 @@ __device__ __forceinline__ void tile_pv_shared(const SplitArgs& a, const Ctx& cx
         }
     }
     if constexpr (EMIT) emit_root<S, MASKED>(a, cx, tt, sc[0]);
-    // V rows are addressed from the K stage: the stage offset, the V tile
-    // and the second 16-row half (same swizzle) are constant offsets of the
-    // read.
-    constexpr int VOFF = SOFF + S::TK * S::ROWB;
-    const int trow0 = cx.ks * 32 + 4 * cx.lj + (cx.li >> 2);
-    const int tsel = (cx.li >> 1) & 1;
-    const char* vrow0 = Ks + trow0 * S::ROWB + 8 * (cx.li & 1);
-    const int sw0 = swz(trow0) ^ tsel;
+    // V rows are addressed from the K stage (vrow0, VOFF above): the stage
+    // offset, the V tile and the second 16-row half (same swizzle) are
+    // constant offsets of the read.
     // V operands go through a window of VW column blocks (two transposed
     // reads each).  The first VW blocks are read before the exponentials, so
     // their latency hides under them; each later block is read as the window
@@ -387,6 +438,30 @@ __device__ __forceinline__ void tile_pv_shared(const SplitArgs& a, const Ctx& cx
     // push the three-block waves of the larger shapes into register spills,
     // so those keep a window of one block read after the exponentials.
     constexpr int VW = NBA >= 3 ? (S::R == 8 ? 1 : 2) : 4;
+    if constexpr (MASKED) {
+        // Masked tiles (at most two per split: the ragged end of a slice and
+        // the tree's own rows): a row here may see only a handful of keys,
+        // whose rounding errors would not average out, so P travels as two
+        // bf16 parts; V column blocks are read one at a time after the
+        // exponentials, which keeps the extra parts within the registers.
+        bf16x8 pb[NBA], pl[NBA];
+#pragma unroll
+        for (int b = 0; b < NBA; ++b)
+            softmax_block<SHIFT, true>(sc[b], c, (SHIFT && m[b] != -INFINITY) ? m[b] : 0.0f, l[b], pb[b], pl[b]);
+#pragma unroll
+        for (int db = 0; db < 8; ++db) {
+            bf16x4 c0 = ds_read_tr16_b64_at<VOFF>(vrow0 + 16 * ((2 * db) ^ sw0));
+            bf16x4 c1 = ds_read_tr16_b64_at<VOFF + 16 * S::ROWB>(vrow0 + 16 * ((2 * db) ^ sw0));
+            lds_wait(c0, c1);
+            const bf16x8 vop = __builtin_shufflevector(c0, c1, 0, 1, 2, 3, 4, 5, 6, 7);
+#pragma unroll
+            for (int b = 0; b < NBA; ++b) {
+                o[b][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pb[b], vop, o[b][db], 0, 0, 0);
+                o[b][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl[b], vop, o[b][db], 0, 0, 0);
+            }
+        }
+        return;
+    }
     if constexpr (VW == 1) {
         bf16x8 pb[NBA];
 #pragma unroll
@@ -790,12 +865,13 @@ __global__ __launch_bounds__(W * 64, 1) void split_mfma(const SplitArgs a) {
     int64_t n_keys = a.n_keys;
     int64_t chunk = a.chunk_keys;
     cx.n_prefix = a.n_prefix;
-    if constexpr (MODE == kModePaged) {
+    constexpr bool PAGED = MODE == kModePaged || MODE == kModePagedGather;
+    if constexpr (PAGED) {
         while (b + 1 < a.B && (int)blockIdx.x >= a.seg_base[b + 1]) ++b;
         cx.split = blockIdx.x - a.seg_base[b];
         seq_splits = a.seg_base[b + 1] - a.seg_base[b];
         cx.n_prefix = a.npb[b];
-        n_keys = cx.n_prefix;
+        n_keys = MODE == kModePagedGather ? a.nib[b] : cx.n_prefix;
         chunk = (n_keys + seq_splits - 1) / seq_splits;
         chunk = (chunk + S::TK - 1) / S::TK * S::TK;
     }
@@ -808,7 +884,7 @@ __global__ __launch_bounds__(W * 64, 1) void split_mfma(const SplitArgs a) {
     const int n_tail_tiles = cx.split == seq_splits - 1 ? (a.T + S::TK - 1) / S::TK : 0;
     cx.n_tiles = cx.n_pre_tiles + n_tail_tiles;
     // paged: this head's rows start g * page_rows rows into every page
-    const size_t head_off = MODE == kModePaged ? (size_t)cx.g * a.page_rows * S::ROWB
+    const size_t head_off = PAGED ? (size_t)cx.g * a.page_rows * S::ROWB
                                                : (size_t)cx.g * (size_t)a.kv_head_stride * 2;
     cx.kbase = (const char*)a.k + head_off;
     cx.vbase = (const char*)a.v + head_off;
@@ -843,6 +919,25 @@ __global__ __launch_bounds__(W * 64, 1) void split_mfma(const SplitArgs a) {
         for (int i = threadIdx.x; i < ntp; i += S::WAVES * 64) idx_lds[cx.npg + i] = table[cx.tpg0 + i];
         __syncthreads();
     }
+    if constexpr (MODE == kModePagedGather) {
+        // this split's index slice and (last split) the tree rows, each
+        // position translated to its pool row through the block table
+        const int32_t* table = a.table + (size_t)b * a.table_stride;
+        const int32_t* list = a.idx + (size_t)b * a.idx_stride;
+        const int n = (int)(cx.c1 > cx.c0 ? cx.c1 - cx.c0 : 0);
+        const uint32_t in_page = (uint32_t)(a.page_rows - 1);
+        for (int i = threadIdx.x; i < n; i += S::WAVES * 64) {
+            const uint32_t pos = (uint32_t)list[cx.c0 + i];
+            idx_lds[i] = (int32_t)(((uint32_t)table[pos >> a.page_shift] << a.page_shift) | (pos & in_page));
+        }
+        if (cx.split == seq_splits - 1)
+            for (int i = threadIdx.x; i < a.T; i += S::WAVES * 64) {
+                const uint64_t pos = (uint64_t)cx.n_prefix + i;
+                idx_lds[kGatherChunkMax + i] =
+                    (int32_t)(((uint32_t)table[pos >> a.page_shift] << a.page_shift) | ((uint32_t)pos & in_page));
+            }
+        __syncthreads();
+    }
 
     // Query blocks are dealt round-robin to the R row groups, so a wave owns
     // NB or NB-1 of them (the planner guarantees it).
@@ -864,6 +959,8 @@ hipError_t launch(int mode, const SplitArgs& a, int n_kv_heads, hipStream_t stre
         hipLaunchKernelGGL((split_mfma<W, R, NB, kModeGather>), grid, dim3(W * 64), 0, stream, a);
     else if (mode == kModePaged)
         hipLaunchKernelGGL((split_mfma<W, R, NB, kModePaged>), grid, dim3(W * 64), 0, stream, a);
+    else if (mode == kModePagedGather)
+        hipLaunchKernelGGL((split_mfma<W, R, NB, kModePagedGather>), grid, dim3(W * 64), 0, stream, a);
     else if (mode == kModeContigRoot)
         hipLaunchKernelGGL((split_mfma<W, R, NB, kModeContigRoot>), grid, dim3(W * 64), 0, stream, a);
     else

@@ -169,7 +169,9 @@ ACCEPT_WORKLOADS = {
 
 @dataclass
 class PagedWorkload:
-    """A batch of sequences sharing one tree shape, K/V in pages of a pool."""
+    """A batch of sequences sharing one tree shape, K/V in pages of a pool.
+    With n_idx set it is the draft pass: sequence b reads an index list of
+    min(n_idx, length) positions (the first n_keep always among them)."""
     name: str
     lengths: tuple
     Hq: int
@@ -178,16 +180,26 @@ class PagedWorkload:
     n_nodes: int
     page_rows: int
     seed: int
+    n_idx: Optional[int] = None
+    n_keep: int = 128
+    tree: str = "kary"
 
     def parent(self) -> np.ndarray:
+        if self.tree == "chain":
+            return chain_parent(self.n_nodes)
         return kary_tree_parent(self.n_nodes, 3)
 
     def pages_needed(self):
         return [-(-(n + self.n_nodes) // self.page_rows) for n in self.lengths]
 
+    def index_lengths(self):
+        return [min(self.n_idx, n) for n in self.lengths] if self.n_idx is not None else None
+
     def kv_bytes(self) -> int:
-        """K+V bytes one call reads: every sequence's prefix plus its tree rows."""
-        return sum(2 * self.Hkv * (n + self.n_nodes) * self.d * 2 for n in self.lengths)
+        """K+V bytes one call reads: every sequence's prefix (or index list)
+        plus its tree rows."""
+        keys = self.index_lengths() or list(self.lengths)
+        return sum(2 * self.Hkv * (n + self.n_nodes) * self.d * 2 for n in keys)
 
 
 PAGED_WORKLOADS = {
@@ -197,7 +209,23 @@ PAGED_WORKLOADS = {
                                                                6400, 4800),
                                     Hq=32, Hkv=8, d=128, n_nodes=full_kary_nodes(3), page_rows=16,
                                     seed=8000),
+    # the draft pass over the same batch: 4096-position partial caches (the
+    # first 128 positions kept), four drafted tokens in a chain
+    "paged_partial_gqa8b_b8": PagedWorkload("paged_partial_gqa8b_b8",
+                                            lengths=(25600, 19200, 16000, 12800, 9600, 8000, 6400, 4800),
+                                            Hq=32, Hkv=8, d=128, n_nodes=4, page_rows=16, seed=8100,
+                                            n_idx=4096, n_keep=128, tree="chain"),
 }
+
+
+def make_paged_index_lists(w: PagedWorkload, device, seed_offset: int = 0):
+    """The draft pass's index lists as one int32 tensor [B, max n_idx], row b
+    holding sequence b's sorted list (entries past its length are -1)."""
+    lens = w.index_lengths()
+    out = np.full((len(lens), max(max(lens), 1)), -1, dtype=np.int32)
+    for b, (n, k) in enumerate(zip(w.lengths, lens)):
+        out[b, :k] = retained_index_set(n, k, w.n_keep, w.seed + seed_offset + 7919 * (b + 1))
+    return torch.from_numpy(out).to(device)
 
 
 def make_paged_inputs(w: PagedWorkload, device, seed_offset: int = 0):
