@@ -376,6 +376,15 @@ int tsw_tree_attn_verify_noalloc(const tsw_attn_desc* desc, const void* q, const
  * TSW_EHIP. */
 int tsw_read_stream(const tsw_attn_desc* desc, const void* k, const void* v, unsigned* sink, tsw_stream_t stream);
 
+/* Measurement aid, not a step of the method: the launch floor of the split
+ * phase.  Launches a kernel that does nothing on the grid, block size and
+ * by-value argument size tsw_tree_attn_verify (n_idx < 0) or
+ * tsw_tree_attn_partial (n_idx >= 0) would use for its split kernel, so
+ * that a caller can time "empty split + merge" beside the real call.
+ * *threads (may be NULL) receives the work-group size.  Errors: as
+ * tsw_plan_splits. */
+int tsw_launch_floor(const tsw_attn_desc* desc, int64_t n_idx, int32_t* threads, tsw_stream_t stream);
+
 /* Static description of a status code. */
 const char* tsw_status_str(int status);
 

@@ -362,3 +362,10 @@ def test_read_stream_argument_errors(L):
     odd = ctypes.c_void_p(0x10008)
     assert L.tsw_read_stream(ctypes.byref(d), odd, FAKE, FAKE, None) == EINVAL
 
+
+
+def test_launch_floor_argument_errors(L):
+    """The launch-floor aid checks its descriptor before any HIP call."""
+    assert L.tsw_launch_floor(ctypes.byref(_desc(T=0)), -1, None, None) == EINVAL
+    assert L.tsw_launch_floor(ctypes.byref(_desc(Hq=3)), -1, None, None) == EINVAL
+    assert L.tsw_launch_floor(ctypes.byref(_desc()), 101, None, None) == EBADINDEX     # n_idx > n_prefix

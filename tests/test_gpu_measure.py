@@ -43,3 +43,25 @@ def test_read_stream_runs_and_is_faster_than_the_call():
     print("read stream %.2f us, verify %.2f us" % (t_read * 1e3, t_call * 1e3), flush=True)
     assert 0.0 < t_read <= t_call
     assert int(sink.sum()) == 0
+
+
+def test_launch_floor_runs_and_is_faster_than_the_call():
+    """The empty split-grid kernel runs and takes less time than the call."""
+    w, q, k, v = _case(60000)
+    fl = tsw.prepare_launch_floor(q, k, w.n_prefix)
+    tsw.tree_attn_verify(q, k, v, w.parent(), w.n_prefix)
+    fl()
+    torch.cuda.synchronize()
+    s = torch.cuda.current_stream()
+    e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    e[0].record(s)
+    for _ in range(5):
+        fl()
+    e[1].record(s)
+    for _ in range(5):
+        tsw.tree_attn_verify(q, k, v, w.parent(), w.n_prefix)
+    e[2].record(s)
+    torch.cuda.synchronize()
+    t_floor, t_call = e[0].elapsed_time(e[1]) / 5, e[1].elapsed_time(e[2]) / 5
+    print("launch floor %.2f us, verify %.2f us" % (t_floor * 1e3, t_call * 1e3), flush=True)
+    assert 0.0 < t_floor < t_call

@@ -19,5 +19,5 @@ from ._binding import (  # noqa: F401
     paged_partial_workspace_size, tree_attn_partial_paged, prepare_partial_paged,
     select_workspace_size, select_partial, prepare_select,
     verify_select_workspace_size, tree_attn_verify_select, prepare_verify_select,
-    read_stream, prepare_read_stream, noalloc_scratch_bytes, tree_attn_verify_noalloc,
+    read_stream, prepare_read_stream, prepare_launch_floor, noalloc_scratch_bytes, tree_attn_verify_noalloc,
 )

@@ -81,6 +81,7 @@ def lib():
     L.tsw_accept_greedy.argtypes = [vp, i32, vp, i64, i32, vp, vp, vp, sz, vp]
     L.tsw_kv_compact.argtypes = [vp, vp, i32, i64, i32, i32, i32, i64, i64, i32, vp, vp]
     L.tsw_read_stream.argtypes = [D, vp, vp, vp, vp]
+    L.tsw_launch_floor.argtypes = [D, i64, vp, vp]
     L.tsw_tree_attn_verify_noalloc.argtypes = [D, vp, vp, vp, vp, vp, vp, vp]
     L.tsw_noalloc_scratch_bytes.argtypes = []
     L.tsw_noalloc_scratch_bytes.restype = ctypes.c_size_t
@@ -90,7 +91,7 @@ def lib():
                  "tsw_tree_attn_verify", "tsw_tree_attn_partial", "tsw_tree_attn_split",
                  "tsw_lse_merge", "tsw_accept_workspace_size", "tsw_accept_greedy",
                  "tsw_kv_compact", "tsw_paged_workspace_size", "tsw_tree_attn_verify_paged",
-                 "tsw_select_workspace_size", "tsw_select_partial", "tsw_read_stream",
+                 "tsw_select_workspace_size", "tsw_select_partial", "tsw_read_stream", "tsw_launch_floor",
                  "tsw_tree_attn_verify_noalloc", "tsw_paged_partial_workspace_size",
                  "tsw_tree_attn_partial_paged"):
         getattr(L, name).restype = ctypes.c_int
@@ -693,6 +694,14 @@ def prepare_read_stream(q, k, v, n_prefix, sink, scale=None, stream=None):
     args = (ctypes.byref(desc), _dev_ptr(k), _dev_ptr(v), _dev_ptr(sink), st)
     return PreparedCall(lib().tsw_read_stream, args, "tsw_read_stream", keep=(desc,))
 
+
+def prepare_launch_floor(q, k, n_prefix, n_idx=None, scale=None, impl="auto", stream=None):
+    """Bound tsw_launch_floor call (a measurement aid): an empty kernel on
+    the split grid of the verify (n_idx None) or partial call."""
+    desc = make_desc(q, k, n_prefix, scale, impl)
+    st = ctypes.c_void_p((stream or torch.cuda.current_stream(q.device)).cuda_stream)
+    args = (ctypes.byref(desc), -1 if n_idx is None else int(n_idx), None, st)
+    return PreparedCall(lib().tsw_launch_floor, args, "tsw_launch_floor", keep=(desc,))
 
 
 def noalloc_scratch_bytes():

@@ -847,6 +847,26 @@ int tsw_read_stream(const tsw_attn_desc* desc, const void* k, const void* v, uns
                                               (hipStream_t)stream));
 }
 
+int tsw_launch_floor(const tsw_attn_desc* desc, int64_t n_idx, int32_t* threads, tsw_stream_t stream) {
+    int rc = check_desc(desc);
+    if (rc != TSW_OK) return rc;
+    if (n_idx > desc->n_prefix) return TSW_EBADINDEX;
+    int cus = 0;
+    rc = device_cus(&cus);
+    if (rc != TSW_OK) return rc;
+    const bool gather = n_idx >= 0;
+    const int64_t n_keys = gather ? n_idx : desc->n_prefix;
+    SplitArgs a;
+    memset(&a, 0, sizeof a);
+    rc = plan(desc, n_keys, gather, cus, &a.n_splits);
+    if (rc != TSW_OK) return rc;
+    tsw::MfmaConfig cfg;
+    // the vector-ALU split kernel runs 256 threads per work-group
+    const int nthreads = use_mfma(desc, n_keys, &cfg) ? cfg.waves * 64 : 256;
+    if (threads) *threads = nthreads;
+    return hip_status(tsw::launch_launch_floor(a, desc->Hkv, nthreads, (hipStream_t)stream));
+}
+
 const char* tsw_status_str(int status) {
     switch (status) {
         case TSW_OK: return "ok";

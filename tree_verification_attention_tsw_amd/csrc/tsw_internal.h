@@ -168,6 +168,11 @@ hipError_t launch_importance_from_scores(const float* root_s, int64_t stride, co
 hipError_t launch_read_stream(const void* k, const void* v, int n_kv_heads, int64_t head_bytes, int64_t rows,
                               int n_splits, unsigned* sink, hipStream_t stream);
 
+// Launch floor (measurement aid): an empty kernel on a split kernel's grid
+// (a.n_splits x n_kv_heads) with `threads` per work-group and a's size of
+// by-value arguments.
+hipError_t launch_launch_floor(const SplitArgs& a, int n_kv_heads, int threads, hipStream_t stream);
+
 // Key tile of the vector-ALU kernel and its query rows per work-group.
 constexpr int kValuTile = 64;
 constexpr int kValuRows = 16;

@@ -323,13 +323,16 @@ __device__ __forceinline__ void merge_pair(int n_splits, int64_t stride, int64_t
     }
 }
 
-// One sequence: n_splits blocks of n_rows rows, two rows per wavefront.
+// One sequence: n_splits blocks of n_rows rows, two rows per wavefront,
+// one wavefront per work-group: the partials are streamed once, and small
+// work-groups spread them over every CU (a CU's share of the reads, not the
+// arithmetic, sets the time).
 template <int CH>
-__global__ __launch_bounds__(256) void lse_merge_pairs(int n_splits, int64_t n_rows, const float* __restrict__ part_o,
-                                                       const float* __restrict__ part_lse, float* __restrict__ o,
-                                                       float* __restrict__ lse) {
+__global__ __launch_bounds__(64) void lse_merge_pairs(int n_splits, int64_t n_rows, const float* __restrict__ part_o,
+                                                      const float* __restrict__ part_lse, float* __restrict__ o,
+                                                      float* __restrict__ lse) {
     const int h = (threadIdx.x >> 5) & 1;
-    const int64_t r = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * 2 + h;
+    const int64_t r = (int64_t)blockIdx.x * 2 + h;
     if (r - h >= n_rows) return;                     // the whole wave is past the end (uniform)
     const bool valid = r < n_rows;
     const int64_t rl = valid ? r : n_rows - 1;
@@ -337,14 +340,15 @@ __global__ __launch_bounds__(256) void lse_merge_pairs(int n_splits, int64_t n_r
 }
 
 // Several sequences with an even number of rows each (so a wavefront's two
-// rows share a run of splits), two rows per wavefront.
+// rows share a run of splits), two rows per wavefront, one wavefront per
+// work-group.
 template <int CH>
-__global__ __launch_bounds__(256) void lse_merge_segs_pairs(const MergeSegs segs, int64_t n_rows,
-                                                            const float* __restrict__ part_o,
-                                                            const float* __restrict__ part_lse,
-                                                            float* __restrict__ o, float* __restrict__ lse) {
+__global__ __launch_bounds__(64) void lse_merge_segs_pairs(const MergeSegs segs, int64_t n_rows,
+                                                           const float* __restrict__ part_o,
+                                                           const float* __restrict__ part_lse,
+                                                           float* __restrict__ o, float* __restrict__ lse) {
     const int h = (threadIdx.x >> 5) & 1;
-    const int64_t r0 = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * 2;
+    const int64_t r0 = (int64_t)blockIdx.x * 2;
     if (r0 >= n_rows) return;                        // uniform
     const int64_t r = r0 + h;                        // r0 even, rows_per_seg even: same run
     const int seg = (int)((uint32_t)r0 / (uint32_t)segs.rows_per_seg);
@@ -433,15 +437,15 @@ hipError_t launch_lse_merge_segs(const MergeSegs& segs, int64_t n_rows, const fl
     // two rows per wavefront when a wavefront's rows always share a run
     // (even rows per sequence) and the 16-byte pieces are aligned
     if (segs.rows_per_seg % 2 == 0 && (((uintptr_t)part_o | (uintptr_t)o) & 15) == 0) {
-        const dim3 pgrid((unsigned)((n_rows + 7) / 8));
+        const dim3 pgrid((unsigned)((n_rows + 1) / 2));
         if (most <= 8)
-            hipLaunchKernelGGL((lse_merge_segs_pairs<8>), pgrid, dim3(256), 0, stream, segs, n_rows, part_o, part_lse,
+            hipLaunchKernelGGL((lse_merge_segs_pairs<8>), pgrid, dim3(64), 0, stream, segs, n_rows, part_o, part_lse,
                                o, lse);
         else if (most <= 16)
-            hipLaunchKernelGGL((lse_merge_segs_pairs<16>), pgrid, dim3(256), 0, stream, segs, n_rows, part_o,
+            hipLaunchKernelGGL((lse_merge_segs_pairs<16>), pgrid, dim3(64), 0, stream, segs, n_rows, part_o,
                                part_lse, o, lse);
         else
-            hipLaunchKernelGGL((lse_merge_segs_pairs<32>), pgrid, dim3(256), 0, stream, segs, n_rows, part_o,
+            hipLaunchKernelGGL((lse_merge_segs_pairs<32>), pgrid, dim3(64), 0, stream, segs, n_rows, part_o,
                                part_lse, o, lse);
         return hipGetLastError();
     }
@@ -467,9 +471,9 @@ hipError_t launch_lse_merge(int n_splits, int64_t n_rows, int d, const float* pa
         // be 16-byte aligned (any alignment takes the row-per-wave kernel)
         const bool aligned16 = (((uintptr_t)part_o | (uintptr_t)o) & 15) == 0;
         if (d == 128 && aligned16) {
-            const dim3 pgrid((unsigned)((n_rows + 7) / 8));
+            const dim3 pgrid((unsigned)((n_rows + 1) / 2));
 #define TSW_MERGE_PAIRS(CH_) \
-    hipLaunchKernelGGL((lse_merge_pairs<CH_>), pgrid, dim3(256), 0, stream, n_splits, n_rows, part_o, part_lse, o, lse)
+    hipLaunchKernelGGL((lse_merge_pairs<CH_>), pgrid, dim3(64), 0, stream, n_splits, n_rows, part_o, part_lse, o, lse)
             if (n_splits <= 8) TSW_MERGE_PAIRS(8);
             else if (n_splits <= 16) TSW_MERGE_PAIRS(16);
             else TSW_MERGE_PAIRS(32);

@@ -1,5 +1,6 @@
-// Read-stream ceiling of the LDS-DMA path (a measurement aid, not a step of
-// the method): streams every K and V row a tree-verification call reads,
+// Measurement aids, not steps of the method.
+//
+// Read-stream ceiling of the LDS-DMA path: streams every K and V row a tree-verification call reads,
 // through the same kind of ring the matrix-core split kernel uses (two
 // 128-key load groups of 64 KB per work-group, each issued in two 32 KB
 // halves, one work-group per (split, kv head)), with no arithmetic.  Its
@@ -63,7 +64,18 @@ __global__ __launch_bounds__(kStreamWaves * 64, 1) void read_stream(const char* 
     if (acc == 0x9e3779b9u) sink[threadIdx.x & 15] = acc;
 }
 
+// Launch floor (a measurement aid): a kernel that does nothing, launched
+// with a split kernel's grid, block and by-value arguments.
+__global__ void launch_floor(const SplitArgs a) {
+    if (a.n_splits < 0 && threadIdx.x == 0) a.part_lse[0] = 0.0f;   // never: keeps the argument live
+}
+
 }  // namespace
+
+hipError_t launch_launch_floor(const SplitArgs& a, int n_kv_heads, int threads, hipStream_t stream) {
+    hipLaunchKernelGGL(launch_floor, dim3(a.n_splits, n_kv_heads), dim3(threads), 0, stream, a);
+    return hipGetLastError();
+}
 
 hipError_t launch_read_stream(const void* k, const void* v, int n_kv_heads, int64_t head_bytes, int64_t rows,
                               int n_splits, unsigned* sink, hipStream_t stream) {
