@@ -223,15 +223,16 @@ def write_counters(dirs, out, kernel, simds, xcds, units_per_simd, unit_name, co
     for c, v in vals.items():
         lines.append("  %-32s %18.1f" % (c, v))
     lines.append("derived (%d SIMDs, %d XCDs, %g %s per SIMD):" % (simds, xcds, units_per_simd, unit_name))
-    clk = None
     if "GRBM_GUI_ACTIVE" in vals:
+        # GRBM_GUI_ACTIVE spans the whole collection window of a dispatch, so
+        # this rate is not taken as the shader clock
         cyc = vals["GRBM_GUI_ACTIVE"] / xcds
-        clk = cyc / (dur * 1e3)
-        lines.append("  clock: GRBM_GUI_ACTIVE / XCDs / duration = %.0f cycles / %.2f us = %.2f GHz" % (cyc, dur, clk))
+        lines.append("  GRBM_GUI_ACTIVE / XCDs / duration = %.0f / %.2f us = %.2f per ns (collection window, "
+                     "not the shader clock)" % (cyc, dur, cyc / (dur * 1e3)))
     if "SQ_VALU_MFMA_BUSY_CYCLES" in vals:
         busy = vals["SQ_VALU_MFMA_BUSY_CYCLES"] / simds
-        lines.append("  MFMA busy cycles per SIMD: %.0f%s" % (
-            busy, " = %.1f%% of the kernel's cycles" % (100.0 * busy / (clk * dur * 1e3)) if clk else ""))
+        lines.append("  MFMA busy cycles per SIMD: %.0f = %.1f%% of the kernel's cycles at 2.4 GHz, %.1f%% at 2.0 GHz"
+                     % (busy, 100.0 * busy / (2.4 * dur * 1e3), 100.0 * busy / (2.0 * dur * 1e3)))
     if "SQ_VALU_MFMA_COEXEC_CYCLES" in vals:
         lines.append("  cycles with an MFMA busy and a VALU instruction issued, per SIMD: %.0f"
                      % (vals["SQ_VALU_MFMA_COEXEC_CYCLES"] / simds))
