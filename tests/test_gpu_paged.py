@@ -245,3 +245,20 @@ def test_paged_partial_bench_workload_all_rows():
         say("  draft bench workload seq %d n_prefix %d n_idx %d: max|dO| %.3g max|dLSE| %.3g (all rows)"
             % (b, n, k, eo, el))
         assert eo <= TOL and el <= TOL, (b, n, eo, el)
+
+
+def test_paged_partial_max_batch_and_degenerate_rows():
+    """64 sequences (the most a call takes), T = 1 (plain decoding), lengths
+    from 0 (no committed positions: the node attends to itself only) up, and
+    index lists from empty to the whole cache."""
+    lengths = [(37 * b) % 700 for b in range(64)]
+    lengths[0], lengths[1] = 0, 1
+    n_idx = [min(n, (53 * b) % 400) for b, n in enumerate(lengths)]
+    n_idx[5] = lengths[5]
+    check_partial_batch(lengths, n_idx, 1, 16, 4, 16, 18, parent=wl.chain_parent(1))
+
+
+def test_paged_verify_max_batch_and_empty_prefix():
+    lengths = [(41 * b) % 900 for b in range(64)]
+    lengths[0] = 0
+    check_batch(lengths, 4, 16, 4, 32, 19, parent=wl.chain_parent(4))

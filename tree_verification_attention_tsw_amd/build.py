@@ -12,8 +12,7 @@ LIB = os.path.join(PKG, "libtsw.so")
 # Matrix-core kernel shapes (waves, row groups, query blocks per wave); each
 # one is its own object compiled from tsw_mfma_inst.hip, so they build in
 # parallel.
-MFMA_SHAPES = [(4, 1, 1), (4, 1, 2), (4, 1, 3), (4, 1, 4), (4, 2, 3), (4, 2, 4), (4, 2, 5), (4, 4, 3), (4, 4, 4),
-               (4, 4, 5), (8, 2, 2), (8, 4, 2), (8, 4, 3), (8, 8, 2), (8, 8, 3)]
+MFMA_SHAPES = [(4, 1, 1), (4, 1, 2), (8, 2, 2), (8, 4, 2), (8, 4, 3), (8, 8, 2), (8, 8, 3)]
 # (source, extra flags, object name)
 UNITS = [(os.path.join(CSRC, n), [], n + ".o")
          for n in ("tsw_api.cpp", "tsw_kernels.hip", "tsw_mfma.hip", "tsw_accept.hip", "tsw_select.hip",

@@ -396,8 +396,10 @@ int vs_layout(const tsw_attn_desc* d, VsLayout* L) {
     rc = plan(d, d->n_prefix, false, cus, &L->n_splits);
     if (rc != TSW_OK) return rc;
     tsw::MfmaConfig cfg;
-    // the kernel writes root scores for head groups of up to 16 (block 0)
-    L->root = use_mfma(d, d->n_prefix, &cfg) && d->Hq / d->Hkv <= 16;
+    // the kernel writes root scores for head groups of up to 16 (block 0);
+    // the 17-24-block shape has no root-score variant (it would spill), so
+    // its selection reads K again
+    L->root = use_mfma(d, d->n_prefix, &cfg) && d->Hq / d->Hkv <= 16 && !(cfg.rgroups == 8 && cfg.nb >= 3);
     L->root_stride = (d->n_prefix + 3) & ~(int64_t)3;
     L->off_root = ws_bytes_for(d, L->n_splits);
     const size_t root_bytes = L->root ? align256((size_t)d->Hq * L->root_stride * sizeof(float)) : 0;

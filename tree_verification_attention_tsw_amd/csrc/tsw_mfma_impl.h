@@ -978,8 +978,11 @@ hipError_t launch(int mode, const SplitArgs& a, int n_kv_heads, hipStream_t stre
         hipLaunchKernelGGL((split_mfma<W, R, NB, kModePaged>), grid, dim3(W * 64), 0, stream, a);
     else if (mode == kModePagedGather)
         hipLaunchKernelGGL((split_mfma<W, R, NB, kModePagedGather>), grid, dim3(W * 64), 0, stream, a);
-    else if (mode == kModeContigRoot)
-        hipLaunchKernelGGL((split_mfma<W, R, NB, kModeContigRoot>), grid, dim3(W * 64), 0, stream, a);
+    else if (mode == kModeContigRoot) {
+        // no root-score variant of the 17-24-block shape (the host never asks)
+        if constexpr (R == 8 && NB >= 3) return hipErrorInvalidValue;
+        else hipLaunchKernelGGL((split_mfma<W, R, NB, kModeContigRoot>), grid, dim3(W * 64), 0, stream, a);
+    }
     else
         hipLaunchKernelGGL((split_mfma<W, R, NB, kModeContig>), grid, dim3(W * 64), 0, stream, a);
     return hipGetLastError();
