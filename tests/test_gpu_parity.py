@@ -142,9 +142,12 @@ def test_workload_partial32_layers():
 # Query rows per kv head M = T * G select the matrix-core shape (blocks of 16
 # rows: 1-2, 3-4, 5-8, 9-12, 13-16, 17-24); each shape is covered, with
 # ragged M and with row groups that own one block fewer than the others.
+# 13 blocks (M = 193..208) take the shared-block arrangement: (40, 5), (52, 4)
+# (13 full blocks), (41, 5), (49, 4) with two kv heads.
 MFMA_SHAPES = [
     (1, 1, 1), (13, 1, 1), (16, 2, 1), (4, 8, 8), (40, 1, 1), (13, 4, 1), (40, 2, 1),
     (23, 4, 1), (40, 3, 1), (33, 4, 1), (40, 4, 1), (47, 4, 1), (64, 3, 1), (40, 5, 1),
+    (52, 4, 1), (41, 5, 1), (49, 4, 2),
     (64, 4, 1), (61, 4, 1), (53, 5, 1), (50, 7, 1), (64, 6, 2),
 ]
 
@@ -384,13 +387,15 @@ def test_planner_fills_the_chip():
     assert s * w.Hkv <= cus and s * w.Hkv > cus // 2
 
 
+@pytest.mark.parametrize("Hq", [32, 40])
 @pytest.mark.parametrize("where", ["first_tile", "late_tile", "tree_row"])
-def test_large_logit_headroom(where):
+def test_large_logit_headroom(where, Hq):
     """A key whose score is ~60 nats above every other score.  When it is
     not in a split's first tile, the fast pass flags its rows and the
     work-group reruns the split with exact row maxima; either way the
-    result must match the oracle."""
-    T, Hq, Hkv, d, npre = 40, 32, 8, 128, 4096
+    result must match the oracle.  Hq = 40 (13 query blocks per kv head)
+    puts flagged rows in the block the four waves share."""
+    T, Hkv, d, npre = 40, 8, 128, 4096
     parent = wl.kary_tree_parent(T, 3)
     q = gen((T, Hq, d), 81, torch.bfloat16)
     k = gen((Hkv, npre + T, d), 82, torch.bfloat16)

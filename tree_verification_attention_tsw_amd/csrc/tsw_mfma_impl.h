@@ -543,8 +543,14 @@ __device__ __forceinline__ void tile_max(const SplitArgs& a, const Ctx& cx, int 
     }
 }
 
-// The work of one wavefront owning NBA query blocks.
-template <class S, int LAYOUT, int NBA, bool EMIT>
+// The work of one wavefront owning NBA query blocks.  SH: 0 normally; in the
+// shared-block arrangement (13 query blocks on the (8,8,2) shape, where whole
+// blocks would load the SIMDs 4/3/3/3) the last block belongs to no row
+// group: waves 4-7 (one per SIMD, one block of their own each) take it on
+// every fourth key tile each, and their four partial results meet in LDS at
+// the end.  SH = 2 for those waves, 1 for the others (which only keep the
+// barrier sequence).
+template <class S, int LAYOUT, int NBA, bool EMIT, int SH = 0>
 __device__ __forceinline__ void run_wave(const SplitArgs& a, const Ctx& cx) {
     constexpr int STAGES = S::STAGES;
     const float c = a.scale_log2;
@@ -553,7 +559,9 @@ __device__ __forceinline__ void run_wave(const SplitArgs& a, const Ctx& cx) {
     // Q^T as the B operand: lane (li, lj) holds query row li of the block,
     // head-dim elements 32*s + 8*lj .. +7.  Rows past M repeat the first row
     // of this head group (their results are never stored).
-    bf16x8 qop[NBA][4];
+    // own blocks 0 .. NBA-1, then (SH == 2) the shared block at index NBA
+    constexpr int NBS = NBA + (SH == 2 ? 1 : 0);
+    bf16x8 qop[NBS][4];
 #pragma unroll
     for (int b = 0; b < NBA; ++b) {
         const int r = (cx.rg + b * S::R) * 16 + cx.li;
@@ -579,16 +587,40 @@ __device__ __forceinline__ void run_wave(const SplitArgs& a, const Ctx& cx) {
         wait_vmcnt<0>();
     }
 
-    float m_run[NBA], l_run[NBA];
-    f32x4 o[NBA][8];
+    float m_run[NBS], l_run[NBS];
+    f32x4 o[NBS][8];
 #pragma unroll
-    for (int b = 0; b < NBA; ++b) {
+    for (int b = 0; b < NBS; ++b) {
         m_run[b] = 0.0f;
         l_run[b] = 0.0f;
 #pragma unroll
         for (int db = 0; db < 8; ++db) o[b][db] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
     bf16x8 kop[2][4], vop[8];
+
+    // the shared block (SH == 2): a context whose row group names it (block
+    // index rg + 0 * R), its Q operands at index NBA
+    Ctx cxs = cx;
+    cxs.rg = ((a.M + 15) >> 4) - 1;
+    const int sh_k = cx.w - 4;                   // this wave's share: tiles t with t % 4 == sh_k
+    if constexpr (SH == 2) {
+        const int r = cxs.rg * 16 + cx.li;
+        const bool ok = r < a.M;
+        const int t = ok ? r / a.G : 0;
+        const int h = cx.g * a.G + (ok ? r % a.G : 0);
+        const bf16x8* src = (const bf16x8*)(cx.q + ((size_t)t * a.Hq + h) * 128 + 8 * cx.lj);
+#pragma unroll
+        for (int s = 0; s < 4; ++s) qop[NBS - 1][s] = src[4 * s];
+    }
+    // views of the own blocks, and of the shared block alone
+    auto& qown = *reinterpret_cast<bf16x8 (*)[NBA][4]>(&qop[0]);
+    auto& mown = *reinterpret_cast<float (*)[NBA]>(&m_run[0]);
+    auto& lown = *reinterpret_cast<float (*)[NBA]>(&l_run[0]);
+    auto& oown = *reinterpret_cast<f32x4 (*)[NBA][8]>(&o[0]);
+    auto& qsh = *reinterpret_cast<bf16x8 (*)[1][4]>(&qop[NBS - 1]);
+    auto& msh = *reinterpret_cast<float (*)[1]>(&m_run[NBS - 1]);
+    auto& lsh = *reinterpret_cast<float (*)[1]>(&l_run[NBS - 1]);
+    auto& osh = *reinterpret_cast<f32x4 (*)[1][8]>(&o[NBS - 1]);
 
     // One pass over the split's tiles; every pass crosses one barrier per
     // load group (plus one at the start of a rerun), identically in all
@@ -626,10 +658,25 @@ __device__ __forceinline__ void run_wave(const SplitArgs& a, const Ctx& cx) {
             constexpr int SOFF = decltype(soff_c)::value;
             if constexpr (MODE == MAXONLY) {
                 load_k<S, SOFF>(Ks, cx, kop);
-                tile_max<S, NBA, MASKED>(a, cx, t, c, kop, qop, m_run);
+                tile_max<S, NBA, MASKED>(a, cx, t, c, kop, qown, mown);
+                if constexpr (SH == 2)
+                    if ((t & 3) == sh_k) tile_max<S, 1, MASKED>(a, cxs, t, c, kop, qsh, msh);
             } else if constexpr (S::WAVES == 8) {
-                tile_pv_shared<S, NBA, MASKED, MODE == EXACT, EMIT && MODE == FAST, SOFF>(a, cx, t, c, Ks, qop, m_run,
-                                                                                         l_run, o);
+                if constexpr (SH == 2 && !MASKED) {
+                    // an unmasked tile does not need the blocks' row
+                    // indices, so on this wave's share the shared block runs
+                    // as one more block of the same tile
+                    if ((t & 3) == sh_k) {
+                        tile_pv_shared<S, NBS, false, MODE == EXACT, false, SOFF>(a, cx, t, c, Ks, qop, m_run, l_run,
+                                                                                  o);
+                        return;
+                    }
+                }
+                tile_pv_shared<S, NBA, MASKED, MODE == EXACT, EMIT && MODE == FAST, SOFF>(a, cx, t, c, Ks, qown, mown,
+                                                                                         lown, oown);
+                if constexpr (SH == 2 && MASKED)
+                    if ((t & 3) == sh_k)
+                        tile_pv_shared<S, 1, true, MODE == EXACT, false, SOFF>(a, cxs, t, c, Ks, qsh, msh, lsh, osh);
             } else {
                 load_k<S, SOFF>(Ks, cx, kop);
                 load_v<S, SOFF>(Ks, cx, vop);
@@ -711,10 +758,27 @@ __device__ __forceinline__ void run_wave(const SplitArgs& a, const Ctx& cx) {
         return xo + ((((cx.rg * S::NB + b) * S::KS + src) * (8 - S::DPW) + k) * 64 + cx.lane);
     };
     auto xml_at = [&](int b, int src) { return xml + ((cx.rg * S::NB + b) * S::KS + src) * 32; };
+    // the shared block's exchange: the four partial O (8 column blocks per
+    // lane) from the start of the ring, then per-row (m, l)
+    f32x4* sxo = (f32x4*)cx.smem;
+    float* sxml = (float*)(cx.smem + 4 * 8 * 64 * 16);
     auto park = [&]() {
         // row sums: each lane summed its own keys; add the four lane groups
 #pragma unroll
         for (int b = 0; b < NBA; ++b) l_run[b] = quad_sum(l_run[b]);
+        if constexpr (SH != 0) {
+            if constexpr (SH == 2) lsh[0] = quad_sum(lsh[0]);
+            barrier_lds();                       // the ring is free
+            if constexpr (SH == 2) {
+#pragma unroll
+                for (int db = 0; db < 8; ++db) sxo[(sh_k * 8 + db) * 64 + cx.lane] = osh[0][db];
+                if (cx.lj == 0) {
+                    sxml[sh_k * 32 + cx.li] = msh[0];
+                    sxml[sh_k * 32 + 16 + cx.li] = lsh[0];
+                }
+            }
+            barrier_lds();
+        }
         if constexpr (S::KS > 1) {
             barrier_lds();
 #pragma unroll
@@ -761,6 +825,20 @@ __device__ __forceinline__ void run_wave(const SplitArgs& a, const Ctx& cx) {
             }
             bad = bad || !(L >= kMinRowSum && L <= 3.0e38f);
         }
+        if constexpr (SH == 2) {
+            // the shared block's rows over all four shares (the fast pass
+            // has m = 0 in every share, so the sums add up)
+            float L = 0.0f;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) L += sxml[k * 32 + 16 + cx.li];
+            bad = bad || !(L >= kMinRowSum && L <= 3.0e38f);
+        }
+    }
+    if constexpr (SH == 2) {
+        float os = 0.0f;
+#pragma unroll
+        for (int db = 0; db < 8; ++db) os += (osh[0][db][0] + osh[0][db][1]) + (osh[0][db][2] + osh[0][db][3]);
+        bad = bad || !(os - os == 0.0f);
     }
     // Work-group vote: a flagged wave sends every wave through the exact
     // path, which keeps the barrier sequence identical across waves.
@@ -772,6 +850,7 @@ __device__ __forceinline__ void run_wave(const SplitArgs& a, const Ctx& cx) {
     if (any_vote) {
 #pragma unroll
         for (int b = 0; b < NBA; ++b) m_run[b] = -INFINITY;
+        msh[0] = -INFINITY;
         pass(std::integral_constant<int, MAXONLY>{});
 #pragma unroll
         for (int b = 0; b < NBA; ++b) {
@@ -779,8 +858,72 @@ __device__ __forceinline__ void run_wave(const SplitArgs& a, const Ctx& cx) {
 #pragma unroll
             for (int db = 0; db < 8; ++db) o[b][db] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
+        lsh[0] = 0.0f;
+#pragma unroll
+        for (int db = 0; db < 8; ++db) osh[0][db] = f32x4{0.f, 0.f, 0.f, 0.f};
         pass(std::integral_constant<int, EXACT>{});
         park();
+    }
+
+    if constexpr (SH == 2) {
+        // The shared block: wave 4 + k finishes column blocks 2k, 2k+1 from
+        // the four parked shares, added in share order; wave 4 writes the LSE.
+        // Weights per row: w_j = 2^(m_j - max m) (0 for a share without a
+        // visible key), L = sum w_j l_j.
+        const int rbase = cxs.rg * 16;
+        auto share_w = [&](int row, float (&wj)[4], float& mmax, float& L) {
+            float mj[4], lj[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                mj[j] = sxml[j * 32 + row];
+                lj[j] = sxml[j * 32 + 16 + row];
+            }
+            mmax = fmaxf(fmaxf(mj[0], mj[1]), fmaxf(mj[2], mj[3]));
+            L = 0.0f;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                wj[j] = mj[j] == -INFINITY ? 0.0f : exp2_fast(mj[j] - mmax);
+                L += wj[j] * lj[j];
+            }
+        };
+        if (sh_k == 0 && cx.lj == 0 && rbase + cx.li < a.M) {
+            float wj[4], mmax, L;
+            share_w(cx.li, wj, mmax, L);
+            const int r = rbase + cx.li;
+            const size_t orow = ((size_t)cx.row0 + r / a.G) * a.Hq + cx.g * a.G + r % a.G;
+            a.part_lse[orow] = L > 0.0f ? (mmax + __log2f(L)) * kLn2 : -INFINITY;
+        }
+        float wq[4][4];
+        float* dst[4];
+        bool row_ok[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int q = 4 * cx.lj + i;
+            float wj[4], mmax, L;
+            share_w(q, wj, mmax, L);
+            const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) wq[i][j] = wj[j] * inv;
+            const int r = rbase + q;
+            row_ok[i] = r < a.M;
+            const int rr = row_ok[i] ? r : rbase;
+            const size_t orow = ((size_t)cx.row0 + rr / a.G) * a.Hq + cx.g * a.G + rr % a.G;
+            dst[i] = a.part_o + orow * 128 + cx.li;
+        }
+#pragma unroll
+        for (int d2 = 0; d2 < 2; ++d2) {
+            const int db = 2 * sh_k + d2;
+            float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const f32x4 x = sxo[(j * 8 + db) * 64 + cx.lane];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) acc[i] += wq[i][j] * x[i];
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                if (row_ok[i]) dst[i][16 * db] = acc[i];
+        }
     }
 
 #pragma unroll
@@ -963,6 +1106,15 @@ __global__ __launch_bounds__(W * 64, 1) void split_mfma(const SplitArgs a) {
     if constexpr (S::R == 1) {
         run_wave<S, MODE, NB, EMIT>(a, cx);
     } else {
+        if constexpr (S::R == 8 && S::NB == 2) {
+            // 13 blocks: whole blocks would load the SIMDs 4/3/3/3; the last
+            // one is shared by waves 4-7 instead (row groups 0-3 keep two)
+            if (nblk == 13) {
+                if (cx.rg < 4) run_wave<S, MODE, 2, EMIT, 1>(a, cx);
+                else run_wave<S, MODE, 1, EMIT, 2>(a, cx);
+                return;
+            }
+        }
         if (nb_act >= NB) run_wave<S, MODE, NB, EMIT>(a, cx);
         else run_wave<S, MODE, NB - 1, EMIT>(a, cx);
     }
