@@ -21,6 +21,17 @@ code.
         --kernel split_mfma --copy-mib 1024 --alg-bytes N --command "..." --command "..."
     python -m tree_verification_attention_tsw_amd.profiling counters OUT DIR... --kernel NAME \\
         --units-per-simd N --unit-name tile --command "..."
+    python -m tree_verification_attention_tsw_amd.profiling power OUT --workload gqa8b_100k \\
+        [--seconds 8] --command "..."
+
+A third kind of record, socket power under a sustained load: a call runs
+back to back for some seconds while ``amd-smi metric`` reports the socket
+power and the graphics clocks.  MI355X holds its socket power at a limit by
+lowering the graphics clock, so at that limit a call's time follows its
+energy rather than its cycle or byte count; the record gives the power, the
+clocks and the energy per call (power x time) of the verify call and, for
+comparison, of the read-stream kernel (the same K/V bytes through the same
+LDS-DMA ring, no arithmetic).
 """
 import argparse
 import collections
@@ -29,6 +40,11 @@ import glob
 import hashlib
 import json
 import os
+import re
+import shutil
+import subprocess
+import threading
+import time
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
@@ -266,6 +282,145 @@ def read_traffic(path):
     return float(kv["traffic_bytes_per_launch"]), kv["source_digest"]
 
 
+def _amd_smi():
+    exe = shutil.which("amd-smi") or "/opt/rocm/bin/amd-smi"
+    return exe if os.path.exists(exe) else None
+
+
+def smi_metric(timeout=30.0):
+    """(socket power W, mean graphics clock MHz, per-XCD clocks) from one
+    `amd-smi metric -p -c` of GPU 0, or None where the tool or a field is
+    missing."""
+    exe = _amd_smi()
+    if exe is None:
+        return None
+    try:
+        r = subprocess.run([exe, "metric", "-g", "0", "-p", "-c"], capture_output=True, text=True, timeout=timeout)
+    except (OSError, subprocess.TimeoutExpired):
+        return None
+    return parse_smi_metric(r.stdout)
+
+
+def parse_smi_metric(text):
+    """(socket power W, mean graphics clock MHz, per-XCD clocks) from the
+    text of `amd-smi metric -p -c`, or None."""
+    m = re.search(r"SOCKET_POWER:\s*([0-9.]+)\s*W", text)
+    clocks = [float(x) for x in re.findall(r"GFX_\d+:\s*\n\s*CLK:\s*([0-9.]+)\s*MHz", text)]
+    if m is None or not clocks:
+        return None
+    return float(m.group(1)), sum(clocks) / len(clocks), clocks
+
+
+def smi_power_limit(timeout=30.0):
+    """The socket power cap in W from `rocm-smi --showmaxpower`, or None."""
+    exe = shutil.which("rocm-smi") or "/opt/rocm/bin/rocm-smi"
+    if not os.path.exists(exe):
+        return None
+    try:
+        r = subprocess.run([exe, "--showmaxpower"], capture_output=True, text=True, timeout=timeout)
+    except (OSError, subprocess.TimeoutExpired):
+        return None
+    return parse_power_cap(r.stdout)
+
+
+def parse_power_cap(text):
+    m = re.search(r"Max Graphics Package Power \(W\):\s*([0-9.]+)", text)
+    return float(m.group(1)) if m else None
+
+
+def sustained(batch, seconds, samples=2, settle=None):
+    """Run `batch()` (launches some calls, synchronises, returns the GPU
+    microseconds per call it measured) back to back for `seconds`, and take
+    `samples` amd-smi readings from a second thread once `settle` seconds
+    (default: half the run) have passed, so the clocks and the power have
+    reached their loaded state.  Returns a dict, or None without amd-smi."""
+    if _amd_smi() is None:
+        return None
+    settle = seconds / 2 if settle is None else settle
+    readings = []
+
+    def sampler():
+        time.sleep(settle)
+        for _ in range(samples):
+            got = smi_metric()
+            if got is not None:
+                readings.append(got)
+
+    th = threading.Thread(target=sampler, daemon=True)
+    per_call = []
+    t0 = time.perf_counter()
+    th.start()
+    while time.perf_counter() - t0 < seconds or th.is_alive():
+        us = batch()
+        if time.perf_counter() - t0 >= settle:
+            per_call.append(us)
+        if time.perf_counter() - t0 > seconds + 120:
+            break
+    th.join(timeout=1.0)
+    if not readings or not per_call:
+        return None
+    watts = sum(r[0] for r in readings) / len(readings)
+    mhz = sum(r[1] for r in readings) / len(readings)
+    per_call.sort()
+    us = per_call[len(per_call) // 2]
+    return {"us_per_call": round(us, 2), "socket_W": round(watts, 1), "gfx_MHz": round(mhz),
+            "gfx_MHz_per_xcd": [round(c) for c in readings[-1][2]], "mJ_per_call": round(watts * us * 1e-3, 2),
+            "samples": len(readings), "seconds": round(time.perf_counter() - t0, 1)}
+
+
+def power_record(w, seconds=6.0, dev="cuda"):
+    """Sustained-load power of one attention workload: the product verify
+    call, then the read-stream kernel over the same caches."""
+    import torch
+    import tree_verification_attention_tsw_amd as tsw
+    from tree_verification_attention_tsw_amd import workloads as wl
+    n_sets = max(2, -(-int(1.5 * 2 ** 30) // w.kv_bytes()))
+    sets = [wl.make_qkv(w, layer=i, device=dev) for i in range(n_sets)]
+    parent = w.parent()
+    q0, k0 = sets[0][0], sets[0][1]
+    o = torch.empty((w.n_nodes, w.Hq, w.d), dtype=torch.float32, device=dev)
+    lse = torch.empty((w.n_nodes, w.Hq), dtype=torch.float32, device=dev)
+    ws = torch.empty(tsw.workspace_size(q0, k0, w.n_prefix), dtype=torch.uint8, device=dev)
+    sink = torch.zeros(64, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+    kinds = {
+        "verify": [tsw.prepare_verify(q, k, v, parent, w.n_prefix, o, lse, ws, stream=stream) for (q, k, v) in sets],
+        "read_stream": [tsw.prepare_read_stream(q, k, v, w.n_prefix, sink, stream=stream) for (q, k, v) in sets],
+    }
+    out = {"workload": w.name, "limit_W": smi_power_limit()}
+    for name, calls in kinds.items():
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        n = 200
+
+        def batch():
+            e0.record(stream)
+            for i in range(n):
+                calls[i % len(calls)]()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) * 1e3 / n
+
+        out[name] = sustained(batch, seconds)
+    return out
+
+
+def write_power(out, workload, seconds, commands):
+    from tree_verification_attention_tsw_amd import workloads as wl
+    rec = power_record(wl.WORKLOADS[workload], seconds)
+    lines = ["# socket power under a sustained load (amd-smi metric -p -c, GPU 0)"]
+    lines += ["command: " + c for c in commands]
+    lines += ["source_digest: %s" % source_digest(), "workload: %s" % workload,
+              "power_limit_W: %s" % rec["limit_W"]]
+    for name in ("verify", "read_stream"):
+        r = rec[name]
+        if r is None:
+            lines.append("%s: amd-smi not available" % name)
+            continue
+        lines.append("%s: %.2f us per call, socket %.1f W, graphics clock %d MHz (per XCD %s), %.2f mJ per call"
+                     % (name, r["us_per_call"], r["socket_W"], r["gfx_MHz"], r["gfx_MHz_per_xcd"], r["mJ_per_call"]))
+    _write(out, lines)
+
+
 def _write(out, lines):
     with open(out, "w") as f:
         f.write("\n".join(lines) + "\n")
@@ -299,10 +454,17 @@ def main():
     c.add_argument("--units-per-simd", type=float, default=1.0)
     c.add_argument("--unit-name", default="launch")
     c.add_argument("--command", action="append", default=[])
+    pw = sub.add_parser("power")
+    pw.add_argument("out")
+    pw.add_argument("--workload", default="gqa8b_100k")
+    pw.add_argument("--seconds", type=float, default=8.0)
+    pw.add_argument("--command", action="append", default=[])
     a = ap.parse_args()
     if a.cmd == "stats":
         win = (a.window[0], int(a.window[1]), int(a.window[2])) if a.window else None
         write_stats(a.dir, a.out, a.command, win, a.bench_log)
+    elif a.cmd == "power":
+        write_power(a.out, a.workload, a.seconds, a.command)
     elif a.cmd == "counters":
         write_counters(a.dirs, a.out, a.kernel, a.simds, a.xcds, a.units_per_simd, a.unit_name, a.command)
     else:
