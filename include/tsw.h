@@ -137,7 +137,9 @@ int tsw_tree_attn_partial(const tsw_attn_desc* desc, const void* q, const void* 
  *                                 no visible key for the row.
  * The last part also holds the tree rows.  n_splits >= 1; parts may be
  * empty.  Combining the parts with tsw_lse_merge gives the verify / partial
- * result; the same merge combines parts computed on different devices. */
+ * result; the same merge combines parts computed on different devices.
+ * On the matrix-core path a contiguous part holds at most 2^23 keys (larger
+ * parts: TSW_EUNSUPPORTED; tsw_plan_splits plans parts within the limit). */
 int tsw_tree_attn_split(const tsw_attn_desc* desc, const void* q, const void* k, const void* v,
                         const int32_t* parent, const int32_t* idx, int64_t n_idx,
                         int32_t n_splits, float* part_o, float* part_lse, tsw_stream_t stream);

@@ -140,6 +140,10 @@ int plan(const tsw_attn_desc* d, int64_t n_keys, bool gather, int cus, int32_t* 
     if (gather) {
         const int64_t need = cdiv(n_keys, tsw::kGatherChunkMax);
         if (s < need) s = need;
+    } else {
+        // (room for the rounding of a part up to whole key tiles)
+        const int64_t need = cdiv(n_keys, tsw::kContigChunkMax - 256);
+        if (s < need) s = need;
     }
     if (s < 1) s = 1;
     if (s > 65535) return TSW_EUNSUPPORTED;
@@ -195,6 +199,7 @@ int run_split(const tsw_attn_desc* d, const void* q, const void* k, const void* 
         const int64_t tk = cfg.tile_keys();
         a.chunk_keys = cdiv(cdiv(n_keys, n_splits), tk) * tk;
         if (gather && a.chunk_keys > tsw::kGatherChunkMax) return TSW_EUNSUPPORTED;
+        if (!gather && a.chunk_keys > tsw::kContigChunkMax) return TSW_EUNSUPPORTED;
         if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v) & 15) return TSW_EINVAL;
         if (d->kv_head_stride % 8) return TSW_EINVAL;
         const int mode = gather ? tsw::kModeGather : (root_s ? tsw::kModeContigRoot : tsw::kModeContig);

@@ -54,6 +54,20 @@ __device__ __forceinline__ int swz(int r) { return ((2 * (r & 7)) | ((r >> 2) & 
 // of a one-work-group-per-CU kernel by 5-11% over the default policy.
 constexpr int kStreamAux = 2;
 
+// Raw buffer resource over `bytes` bytes from `base` (stride 0, 32-bit data
+// format word): loads at offsets past the range return zeros and never
+// fault, so a ragged tile needs no clamping of its row addresses.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// One LDS-DMA load of 16 bytes per lane from buffer r at voff + soff (bytes)
+// into LDS at dst (uniform), with the streaming hint.
+__device__ __forceinline__ void buffer_load_lds16(__amdgpu_buffer_rsrc_t r, char* dst, uint32_t voff, uint32_t soff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)dst, 16, voff, soff, 0,
+                                             kStreamAux);
+}
+
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
     static_assert(N >= 0 && N < 64, "vmcnt range");

@@ -76,6 +76,11 @@ struct MfmaConfig {
 // Largest index-list slice one work-group stages in LDS (gather variant).
 constexpr int kGatherChunkMax = 4096;
 
+// Largest prefix slice of one work-group in the contiguous layout: its K and
+// V rows are read through buffer resources with 32-bit byte offsets from the
+// slice's first row (256-byte rows, plus the tree rows in the last split).
+constexpr int64_t kContigChunkMax = (int64_t)1 << 23;
+
 // Picks the matrix-core shape for M query rows per kv head; returns false
 // when no shape covers M (callers then use the vector-ALU kernel).
 bool mfma_config_for(int M, MfmaConfig* cfg);

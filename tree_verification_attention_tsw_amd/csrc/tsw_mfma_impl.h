@@ -107,6 +107,9 @@ struct Ctx {
     int64_t n_prefix;            // this sequence's committed length
     int64_t c0, c1;      // prefix key range [c0, c1) of this split
     int64_t pg0, tpg0;   // paged: first page of the slice and of the tree rows
+    const char* kseg;    // contiguous: the split's first K and V rows, and the
+    const char* vseg;    // bytes from there it reads (its slice, plus the
+    uint32_t seg_bytes;  // tree rows in the last split)
     int64_t row0;        // partial-output row of (split, sequence, node 0)
     int npg;             // paged: pages staged for the slice
     int n_pre_tiles, n_tiles;
@@ -122,11 +125,17 @@ __device__ __forceinline__ void issue_tile(const SplitArgs& a, const Ctx& cx, in
     char* sbase = cx.smem + st * S::STAGE;
     const bool pre = tt < cx.n_pre_tiles;
     const int64_t k0 = cx.c0 + (int64_t)tt * S::TK;
-    if (MODE == kModeContig && pre && k0 + S::TK <= cx.c1) {
-        // Whole tile of consecutive cache rows: a uniform base per tile and a
-        // fixed 32-bit offset per lane and instruction.
-        const char* kt = cx.kbase + k0 * S::ROWB;
-        const char* vt = cx.vbase + k0 * S::ROWB;
+    if constexpr (MODE == kModeContig) {
+        // Consecutive cache rows, prefix and tree tiles alike: buffer loads
+        // over the split's rows, a scalar offset per tile (its first row)
+        // and a fixed 32-bit offset per lane and instruction, so a load costs
+        // no vector instruction.  Rows past the split's range (the ragged
+        // end of the slice, the tree tile's padding) read as zeros; their
+        // scores are masked to -inf.
+        const __amdgpu_buffer_rsrc_t krs = raw_rsrc(cx.kseg, cx.seg_bytes);
+        const __amdgpu_buffer_rsrc_t vrs = raw_rsrc(cx.vseg, cx.seg_bytes);
+        const uint32_t r0 = pre ? (uint32_t)tt * S::TK
+                                : (uint32_t)(cx.n_prefix - cx.c0) + (uint32_t)(tt - cx.n_pre_tiles) * S::TK;
 #pragma unroll
         for (int i = 0; i < S::NI; ++i) {
             const int u = cx.w * S::NI + i;
@@ -135,9 +144,7 @@ __device__ __forceinline__ void issue_tile(const SplitArgs& a, const Ctx& cx, in
             const int row = grp * 4 + cx.lj;
             const uint32_t off = (uint32_t)(row * S::ROWB + 16 * (cx.li ^ swz(row)));
             char* dst = sbase + (isv ? S::TK * S::ROWB : 0) + grp * 1024;
-            __builtin_amdgcn_global_load_lds((const void*)((isv ? vt : kt) + off),
-                                             (__attribute__((address_space(3))) void*)dst, 16, 0,
-                                             kStreamAux);
+            buffer_load_lds16(isv ? vrs : krs, dst, off, r0 * (uint32_t)S::ROWB);
         }
         return;
     }
@@ -1048,6 +1055,11 @@ __global__ __launch_bounds__(W * 64, 1) void split_mfma(const SplitArgs a) {
                                                : (size_t)cx.g * (size_t)a.kv_head_stride * 2;
     cx.kbase = (const char*)a.k + head_off;
     cx.vbase = (const char*)a.v + head_off;
+    // contiguous: the split's rows [c0, c1), and in the last split the tree
+    // rows after the prefix (the host keeps this under 4 GB)
+    cx.kseg = cx.kbase + cx.c0 * S::ROWB;
+    cx.vseg = cx.vbase + cx.c0 * S::ROWB;
+    cx.seg_bytes = (uint32_t)(((n_tail_tiles ? cx.n_prefix + a.T : cx.c1) - cx.c0) * S::ROWB);
     int32_t* idx_lds = (int32_t*)(smem + S::RING);
     cx.idx_lds = idx_lds;
     uint64_t* mask_lds = (uint64_t*)(smem + MASK_OFF);

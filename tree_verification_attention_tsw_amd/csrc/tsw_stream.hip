@@ -17,9 +17,10 @@ constexpr int kStreamTile = 64;                      // keys per half group
 constexpr int kStreamTileBytes = 2 * kStreamTile * 256;   // K tile + V tile
 constexpr int kStreamLoads = kStreamTile / 2 / kStreamWaves;  // 1 KB loads per wave per tile
 
-// rows [c0, c1) of one kv head's K and V (256-byte rows), tile t into
-// stage st; rows past c1 re-read row c1 - 1
-__device__ __forceinline__ void stream_issue(const char* kh, const char* vh, int64_t c0, int64_t c1, int t, int st,
+// rows [c0, c1) of one kv head's K and V (256-byte rows; buffers krs / vrs
+// start at row c0 and end at row c1), tile t into stage st; rows past c1
+// read as zeros
+__device__ __forceinline__ void stream_issue(__amdgpu_buffer_rsrc_t krs, __amdgpu_buffer_rsrc_t vrs, int t, int st,
                                              char* smem, int w, int lane) {
     char* sbase = smem + st * kStreamTileBytes;
 #pragma unroll
@@ -27,12 +28,9 @@ __device__ __forceinline__ void stream_issue(const char* kh, const char* vh, int
         const int u = w * kStreamLoads + i;
         const bool isv = u >= kStreamTile / 4;
         const int grp = isv ? u - kStreamTile / 4 : u;
-        int64_t row = c0 + (int64_t)t * kStreamTile + grp * 4 + (lane >> 4);
-        if (row >= c1) row = c1 - 1;
-        const char* src = (isv ? vh : kh) + row * 256 + 16 * (lane & 15);
+        const uint32_t off = (uint32_t)((grp * 4 + (lane >> 4)) * 256 + 16 * (lane & 15));
         char* dst = sbase + (isv ? kStreamTile * 256 : 0) + grp * 1024;
-        __builtin_amdgcn_global_load_lds((const void*)src, (__attribute__((address_space(3))) void*)dst, 16, 0,
-                                         kStreamAux);
+        buffer_load_lds16(isv ? vrs : krs, dst, off, (uint32_t)t * kStreamTile * 256);
     }
 }
 
@@ -47,16 +45,18 @@ __global__ __launch_bounds__(kStreamWaves * 64, 1) void read_stream(const char* 
     const int64_t c1 = c0 + chunk < rows ? c0 + chunk : rows;
     if (c0 >= c1) return;                                  // uniform: an empty split
     const int n = (int)((c1 - c0 + kStreamTile - 1) / kStreamTile);
+    const __amdgpu_buffer_rsrc_t krs = raw_rsrc(kh + c0 * 256, (uint32_t)((c1 - c0) * 256));
+    const __amdgpu_buffer_rsrc_t vrs = raw_rsrc(vh + c0 * 256, (uint32_t)((c1 - c0) * 256));
     // two groups of two tiles in the ring; a group's tiles are issued one
     // per tile of the group before it
-    for (int t = 0; t < 2 && t < n; ++t) stream_issue(kh, vh, c0, c1, t, t, smem, w, lane);
+    for (int t = 0; t < 2 && t < n; ++t) stream_issue(krs, vrs, t, t, smem, w, lane);
     unsigned acc = 0;
     for (int t = 0; t < n; t += 2) {
         wait_vmcnt<0>();
         barrier_lds();
-        if (t + 2 < n) stream_issue(kh, vh, c0, c1, t + 2, (t + 2) % 4, smem, w, lane);
+        if (t + 2 < n) stream_issue(krs, vrs, t + 2, (t + 2) % 4, smem, w, lane);
         acc ^= *(volatile unsigned*)(smem + (t % 4) * kStreamTileBytes + threadIdx.x * 4);
-        if (t + 3 < n) stream_issue(kh, vh, c0, c1, t + 3, (t + 3) % 4, smem, w, lane);
+        if (t + 3 < n) stream_issue(krs, vrs, t + 3, (t + 3) % 4, smem, w, lane);
         if (t + 1 < n) acc ^= *(volatile unsigned*)(smem + ((t + 1) % 4) * kStreamTileBytes + threadIdx.x * 4);
     }
     wait_vmcnt<0>();
