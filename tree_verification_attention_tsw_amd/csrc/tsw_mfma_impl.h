@@ -198,8 +198,39 @@ __device__ __forceinline__ void issue_tile(const SplitArgs& a, const Ctx& cx, in
                                              kStreamAux);
         }
     } else {
-        // paged: every load's page number is read from the staged table
-        // first, then each address is one multiply-add on it
+        if (pre && k0 + S::TK <= cx.c1) {
+            // A whole prefix tile: an instruction's four rows start at a
+            // multiple of four, so they share a page (pages hold at least 16
+            // rows).  Its page number is read once (a uniform LDS read) and
+            // the load goes through a buffer over this head's rows of that
+            // page: a scalar base and row offset per instruction, a fixed
+            // 32-bit offset per lane, no vector address arithmetic.
+            uint32_t page[S::NI];
+#pragma unroll
+            for (int i = 0; i < S::NI; ++i) {
+                const int u = cx.w * S::NI + i;
+                const int grp = u >= S::TK / 4 ? u - S::TK / 4 : u;
+                page[i] = (uint32_t)cx.idx_lds[(int)(((k0 + grp * 4) >> a.page_shift) - cx.pg0)];
+            }
+            const uint32_t head_rows_bytes = (uint32_t)a.page_rows * S::ROWB;
+#pragma unroll
+            for (int i = 0; i < S::NI; ++i) {
+                const int u = cx.w * S::NI + i;
+                const bool isv = u >= S::TK / 4;
+                const int grp = isv ? u - S::TK / 4 : u;
+                const uint32_t pg = __builtin_amdgcn_readfirstlane(page[i]);
+                const char* pbase = (isv ? cx.vbase : cx.kbase) + (uint64_t)pg * (uint64_t)a.page_bytes;
+                const uint32_t r0 = (uint32_t)((k0 + grp * 4) & (a.page_rows - 1));
+                const int row = grp * 4 + cx.lj;
+                const uint32_t off = (uint32_t)(cx.lj * S::ROWB + 16 * (cx.li ^ swz(row)));
+                char* dst = sbase + (isv ? S::TK * S::ROWB : 0) + grp * 1024;
+                buffer_load_lds16(raw_rsrc(pbase, head_rows_bytes), dst, off, r0 * (uint32_t)S::ROWB);
+            }
+            return;
+        }
+        // paged, other tiles (the ragged end of a slice, the tree rows):
+        // every load's page number is read from the staged table first, then
+        // each address is one multiply-add on it
         int64_t pos[S::NI];
         uint32_t page[S::NI];
 #pragma unroll
