@@ -191,6 +191,29 @@ def test_rows_beyond_cache_are_not_read():
                                                                   device=kb.device), float("nan")))
 
 
+@pytest.mark.parametrize("n_splits", [1, 3, 7])
+def test_ragged_splits_do_not_read_past_their_rows(n_splits):
+    """Every split of a contiguous cache reads its own rows (and the last
+    split the tree rows) through a buffer over exactly those rows: the
+    ragged end of each slice and the tree tile's padding read as zeros.
+    K and V rows past n_prefix + T hold NaN and must not leak, whatever
+    the split count (ragged slices in every split)."""
+    T, Hq, Hkv, d, npre, extra = 13, 8, 2, 128, 1001, 200
+    parent = wl.kary_tree_parent(T, 3)
+    q = gen((T, Hq, d), 71, torch.bfloat16)
+    k = gen((Hkv, npre + T + extra, d), 72, torch.bfloat16)
+    v = gen((Hkv, npre + T + extra, d), 73, torch.bfloat16)
+    k[:, npre + T:] = float("nan")
+    v[:, npre + T:] = float("nan")
+    po, pl = tsw.tree_attn_split(q, k, v, parent, npre, n_splits, impl="mfma")
+    o, lse = tsw.lse_merge(po, pl)
+    torch.cuda.synchronize()
+    o_ref, l_ref = oracle.tree_attn(wl.oracle_view(q), wl.oracle_view(k[:, :npre + T]),
+                                    wl.oracle_view(v[:, :npre + T]), parent, npre, 1 / np.sqrt(d),
+                                    nthreads=NTHREADS)
+    check(o, lse, o_ref, l_ref, TOL["bf16"], "ragged splits %d" % n_splits)
+
+
 @pytest.mark.parametrize("n_idx", [0, 1, 100, 4096, 5000])
 def test_partial_sizes(n_idx):
     npre = 20000
