@@ -151,6 +151,16 @@ def test_split_and_merge_argument_errors(L):
     assert L.tsw_lse_merge(2, 0, 128, None, None, None, None, None) == TSW_OK
 
 
+def test_contiguous_part_size_limit(L):
+    # a matrix-core part of a contiguous cache reads its rows through 32-bit
+    # buffer offsets: more than 2^23 keys in one part is refused on the host
+    npre = (1 << 23) + 100
+    d = _desc(n_prefix=npre, kv_head_stride=(npre + 13) * 128, impl=tsw.IMPL["mfma"])
+    p = PARENT.ctypes.data_as(ctypes.c_void_p)
+    assert L.tsw_tree_attn_split(ctypes.byref(d), FAKE, FAKE, FAKE, p, None, 0, 1, FAKE, FAKE,
+                                 None) == EUNSUP
+
+
 def test_null_workspace(L):
     assert _verify(L, _desc(), ws=None) == EINVAL
 
