@@ -288,12 +288,14 @@ def test_non_ancestor_tree_rows_do_not_leak():
     k2[:, [npre + j for j in others], :] = 1e4
     o2, l2 = tsw.tree_attn_verify(q, k2, v, parent, npre)
     torch.cuda.synchronize()
-    # Nodes 39 and 0 see none of the poisoned rows.  (The poisoned scores can
-    # send the work-group through the exact two-pass path, so the unaffected
-    # rows may differ by rounding, not by more.)
+    # Nodes 39 and 0 see none of the poisoned rows.  (The poisoned scores
+    # send the last split's work-group through the exact two-pass path, which
+    # rounds each p to bf16 relative to the row maximum instead of 2^0: the
+    # unaffected rows may differ by that rounding, about 2^-9 of their
+    # values, while a leaked 1e4 key would move them by the size of V.)
     for node in (39, 0):
-        assert float((o1[node] - o2[node]).abs().max()) <= 1e-4
-        assert float((l1[node] - l2[node]).abs().max()) <= 1e-4
+        assert float((o1[node] - o2[node]).abs().max()) <= 1e-3
+        assert float((l1[node] - l2[node]).abs().max()) <= 1e-3
     # nodes that do see poisoned rows change; all rows must match the oracle
     o_ref, l_ref = oracle.tree_attn(wl.oracle_view(q), wl.oracle_view(k2), wl.oracle_view(v),
                                     parent, npre, 1 / np.sqrt(d), nthreads=NTHREADS)

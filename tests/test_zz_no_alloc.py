@@ -49,9 +49,10 @@ def test_noalloc_matches_verify_twice_then_smaller():
 
 
 def test_noalloc_rejects_too_large():
-    # 384 query rows on one kv head over a long cache: one split per CU, and
-    # 256 splits x 64 nodes x 6 heads x 129 floats need more than 32 MiB
-    T, Hq, n_prefix = 64, 6, 32768
+    # 384 query rows on one kv head over a long cache (long enough that the
+    # planner's floor of 3 x 384 keys per split still allows one split per
+    # CU): 256 splits x 64 nodes x 6 heads x 129 floats need more than 32 MiB
+    T, Hq, n_prefix = 64, 6, 300000
     q = torch.zeros((T, Hq, 128), dtype=torch.bfloat16, device="cuda")
     k = torch.zeros((1, n_prefix + T, 128), dtype=torch.bfloat16, device="cuda")
     need = tsw.workspace_size(q, k, n_prefix)

@@ -125,6 +125,11 @@ int plan(const tsw_attn_desc* d, int64_t n_keys, bool gather, int cus, int32_t* 
         s = smax;
         const int64_t by_len = cdiv(n_keys, 2 * tk);
         if (s > by_len) s = by_len;
+        // Every split writes M partial rows of d floats that the merge reads
+        // back; below about 3M keys per split that traffic outweighs the
+        // split's own K/V bytes (short caches), so take fewer, longer splits.
+        const int64_t by_out = n_keys / (3 * (int64_t)d->T * (d->Hq / d->Hkv));
+        if (s > by_out) s = by_out;
         if (s < 1) s = 1;
         const int64_t tt = cdiv(d->T, tk);
         if (n_keys > 0 && s + 1 <= smax &&
