@@ -22,7 +22,7 @@ code.
     python -m tree_verification_attention_tsw_amd.profiling counters OUT DIR... --kernel NAME \\
         --units-per-simd N --unit-name tile --command "..."
     python -m tree_verification_attention_tsw_amd.profiling power OUT --workload gqa8b_100k \\
-        [--seconds 8] --command "..."
+        [--seconds 8] [--half-grid] --command "..."
 
 A third kind of record, socket power under a sustained load: a call runs
 back to back for some seconds while ``amd-smi metric`` reports the socket
@@ -404,6 +404,60 @@ def power_record(w, seconds=6.0, dev="cuda"):
     return out
 
 
+def half_grid_record(w, seconds=6.0, dev="cuda", n_splits=32):
+    """The split kernel alone, sustained, on the workload's grid (n_splits x
+    Hkv work-groups) and on half of it: half the kv heads and query heads,
+    so every work-group keeps its rows and keys but half the CUs idle."""
+    import torch
+    import tree_verification_attention_tsw_amd as tsw
+    from tree_verification_attention_tsw_amd import workloads as wl
+    out = {}
+    for name, hkv in (("full_grid", w.Hkv), ("half_grid", w.Hkv // 2), ("full_grid_again", w.Hkv),
+                      ("half_grid_again", w.Hkv // 2)):
+        ww = wl.Workload(w.name + "_hkv%d" % hkv, Hq=w.G * hkv, Hkv=hkv, d=w.d, n_prefix=w.n_prefix,
+                         n_nodes=w.n_nodes, dtype=w.dtype, seed=w.seed, outliers=w.outliers)
+        n_sets = max(2, -(-int(1.5 * 2 ** 30) // ww.kv_bytes()))
+        sets = [wl.make_qkv(ww, layer=i, device=dev) for i in range(n_sets)]
+        po = torch.empty((n_splits, ww.n_nodes, ww.Hq, ww.d), dtype=torch.float32, device=dev)
+        pl = torch.empty((n_splits, ww.n_nodes, ww.Hq), dtype=torch.float32, device=dev)
+        stream = torch.cuda.current_stream()
+        calls = [tsw.prepare_split(q, k, v, ww.parent(), ww.n_prefix, n_splits, po, pl, stream=stream)
+                 for (q, k, v) in sets]
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+        def batch():
+            e0.record(stream)
+            for i in range(200):
+                calls[i % len(calls)]()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) * 1e3 / 200
+
+        r = sustained(batch, seconds)
+        if r is not None:
+            r["work_groups"] = n_splits * hkv
+        out[name] = r
+        del sets, calls, po, pl
+        torch.cuda.empty_cache()
+    return out
+
+
+def write_half_grid(out, workload, seconds, commands):
+    from tree_verification_attention_tsw_amd import workloads as wl
+    rec = half_grid_record(wl.WORKLOADS[workload], seconds)
+    lines = ["# split kernel alone, sustained: the workload's grid and half of it (half the kv and query",
+             "# heads: the same rows and keys per work-group, half the CUs idle); amd-smi metric -p -c, GPU 0"]
+    lines += ["command: " + c for c in commands]
+    lines += ["source_digest: %s" % source_digest(), "workload: %s" % workload]
+    for name, r in rec.items():
+        if r is None:
+            lines.append("%s: amd-smi not available" % name)
+            continue
+        lines.append("%s: %d work-groups, %.2f us per launch, socket %.1f W, graphics clock %d MHz, %.2f mJ per launch"
+                     % (name, r["work_groups"], r["us_per_call"], r["socket_W"], r["gfx_MHz"], r["mJ_per_call"]))
+    _write(out, lines)
+
+
 def write_power(out, workload, seconds, commands):
     from tree_verification_attention_tsw_amd import workloads as wl
     rec = power_record(wl.WORKLOADS[workload], seconds)
@@ -459,12 +513,17 @@ def main():
     pw.add_argument("--workload", default="gqa8b_100k")
     pw.add_argument("--seconds", type=float, default=8.0)
     pw.add_argument("--command", action="append", default=[])
+    pw.add_argument("--half-grid", action="store_true",
+                    help="the split kernel alone on the workload's grid and on half of it")
     a = ap.parse_args()
     if a.cmd == "stats":
         win = (a.window[0], int(a.window[1]), int(a.window[2])) if a.window else None
         write_stats(a.dir, a.out, a.command, win, a.bench_log)
     elif a.cmd == "power":
-        write_power(a.out, a.workload, a.seconds, a.command)
+        if a.half_grid:
+            write_half_grid(a.out, a.workload, a.seconds, a.command)
+        else:
+            write_power(a.out, a.workload, a.seconds, a.command)
     elif a.cmd == "counters":
         write_counters(a.dirs, a.out, a.kernel, a.simds, a.xcds, a.units_per_simd, a.unit_name, a.command)
     else:
