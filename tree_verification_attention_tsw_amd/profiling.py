@@ -404,16 +404,19 @@ def power_record(w, seconds=6.0, dev="cuda"):
     return out
 
 
-def half_grid_record(w, seconds=6.0, dev="cuda", n_splits=32):
+def half_grid_record(w, seconds=6.0, dev="cuda", n_splits=32, repeat=False):
     """The split kernel alone, sustained, on the workload's grid (n_splits x
     Hkv work-groups) and on half of it: half the kv heads and query heads,
-    so every work-group keeps its rows and keys but half the CUs idle."""
+    so every work-group keeps its rows and keys but half the CUs idle
+    (repeat: both once more, alternating)."""
     import torch
     import tree_verification_attention_tsw_amd as tsw
     from tree_verification_attention_tsw_amd import workloads as wl
     out = {}
-    for name, hkv in (("full_grid", w.Hkv), ("half_grid", w.Hkv // 2), ("full_grid_again", w.Hkv),
-                      ("half_grid_again", w.Hkv // 2)):
+    runs = [("full_grid", w.Hkv), ("half_grid", w.Hkv // 2)]
+    if repeat:
+        runs += [("full_grid_again", w.Hkv), ("half_grid_again", w.Hkv // 2)]
+    for name, hkv in runs:
         ww = wl.Workload(w.name + "_hkv%d" % hkv, Hq=w.G * hkv, Hkv=hkv, d=w.d, n_prefix=w.n_prefix,
                          n_nodes=w.n_nodes, dtype=w.dtype, seed=w.seed, outliers=w.outliers)
         n_sets = max(2, -(-int(1.5 * 2 ** 30) // ww.kv_bytes()))
@@ -444,7 +447,7 @@ def half_grid_record(w, seconds=6.0, dev="cuda", n_splits=32):
 
 def write_half_grid(out, workload, seconds, commands):
     from tree_verification_attention_tsw_amd import workloads as wl
-    rec = half_grid_record(wl.WORKLOADS[workload], seconds)
+    rec = half_grid_record(wl.WORKLOADS[workload], seconds, repeat=True)
     lines = ["# split kernel alone, sustained: the workload's grid and half of it (half the kv and query",
              "# heads: the same rows and keys per work-group, half the CUs idle); amd-smi metric -p -c, GPU 0"]
     lines += ["command: " + c for c in commands]
