@@ -40,14 +40,16 @@ __device__ __forceinline__ float quad_sum(float x) {
     return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
-// 16-byte chunk swizzle of a 256-byte LDS row.  Logical chunk c of tile row r
-// lives in physical slot c ^ swz(r).  For any 8 (and 16) consecutive aligned
-// rows the slots of one logical chunk are all different, and for any 4
-// (and 8) consecutive aligned rows the chunk pairs {2b, 2b+1} land in
-// different slot pairs, so both the K operand reads (one chunk of 16 rows)
-// and the transposed V reads (two chunks of 4 rows per 16 lanes) are free of
-// bank conflicts whether the LDS serves 128 or 256 bytes per clock.
+// 16-byte chunk swizzles of 256-byte LDS rows: logical chunk c of tile row r
+// lives in physical slot c ^ swz(r) (V rows) or c ^ swz_k(r) (K rows).
+// V: for any 4 (and 8) consecutive aligned rows the chunk pairs {2b, 2b+1}
+// land in different slot pairs, so the transposed V reads (two chunks of 4
+// rows per 16 lanes) are free of bank conflicts.  K: a K operand read takes
+// chunk 4s + lj of rows 0..15 (lane li, lj); with the slot XORed by the
+// row's low four bits the read is conflict-free on gfx950, where the V
+// swizzle cost it 4 conflict cycles per instruction (SQ_LDS_BANK_CONFLICT).
 __device__ __forceinline__ int swz(int r) { return ((2 * (r & 7)) | ((r >> 2) & 1)) ^ ((r >> 3) & 1); }
+__device__ __forceinline__ int swz_k(int r) { return r & 15; }
 
 // Cache policy for K/V rows that a call reads exactly once: the non-temporal
 // (streaming) hint.  On MI355X it raises the aggregate LDS-DMA streaming rate

@@ -94,6 +94,7 @@ struct Shape {
     static constexpr int SMEM = LOOP_BYTES > XBYTES ? LOOP_BYTES : XBYTES;
     static_assert(STAGES <= STAGES_FIT, "two load groups fit the LDS");
     static_assert(GT * NI < 64, "vmcnt range");
+    static_assert((TK / 4) % NI == 0, "a wave's loads are all K rows or all V rows");
 };
 
 struct Ctx {
@@ -118,11 +119,17 @@ struct Ctx {
 
 // Issue the DMA loads of tile tt into ring stage st.  One instruction moves
 // four 256-byte rows (64 lanes x 16 bytes) into consecutive LDS; lane (li,
-// lj) of instruction i writes logical chunk li ^ swz(row) of its row.  Rows
+// lj) of instruction i writes logical chunk li ^ swz(row) (V) or li ^ swz_k(row)
+// (K) of its row.  Rows
 // past the slice end re-read a valid row (their scores are masked to -inf).
 template <class S, int MODE>
 __device__ __forceinline__ void issue_tile(const SplitArgs& a, const Ctx& cx, int tt, int st) {
     char* sbase = cx.smem + st * S::STAGE;
+    // waves 0 .. W/2-1 load K rows, the others V rows (uniform per wave);
+    // their LDS rows have different swizzles
+    const bool wave_v = cx.w * S::NI >= S::TK / 4;
+    const int v_bits = wave_v ? 15 : 0;
+    auto row_swz = [&](int row) { return swz_k(row) ^ ((swz(row) ^ swz_k(row)) & v_bits); };
     const bool pre = tt < cx.n_pre_tiles;
     const int64_t k0 = cx.c0 + (int64_t)tt * S::TK;
     if constexpr (MODE == kModeContig) {
@@ -139,10 +146,10 @@ __device__ __forceinline__ void issue_tile(const SplitArgs& a, const Ctx& cx, in
 #pragma unroll
         for (int i = 0; i < S::NI; ++i) {
             const int u = cx.w * S::NI + i;
-            const bool isv = u >= S::TK / 4;
+            const bool isv = wave_v;
             const int grp = isv ? u - S::TK / 4 : u;
             const int row = grp * 4 + cx.lj;
-            const uint32_t off = (uint32_t)(row * S::ROWB + 16 * (cx.li ^ swz(row)));
+            const uint32_t off = (uint32_t)(row * S::ROWB + 16 * (cx.li ^ (isv ? swz(row) : swz_k(row))));
             char* dst = sbase + (isv ? S::TK * S::ROWB : 0) + grp * 1024;
             buffer_load_lds16(isv ? vrs : krs, dst, off, r0 * (uint32_t)S::ROWB);
         }
@@ -155,7 +162,7 @@ __device__ __forceinline__ void issue_tile(const SplitArgs& a, const Ctx& cx, in
 #pragma unroll
         for (int i = 0; i < S::NI; ++i) {
             const int u = cx.w * S::NI + i;
-            const bool isv = u >= S::TK / 4;
+            const bool isv = wave_v;
             const int grp = isv ? u - S::TK / 4 : u;
             const int row = grp * 4 + cx.lj;
             int slot;
@@ -170,7 +177,8 @@ __device__ __forceinline__ void issue_tile(const SplitArgs& a, const Ctx& cx, in
             }
             const uint32_t prow = (uint32_t)cx.idx_lds[slot];
             const char* src = (isv ? cx.vbase : cx.kbase) + (uint64_t)(prow >> a.page_shift) * (uint64_t)a.page_bytes +
-                              (uint32_t)((prow & (uint32_t)(a.page_rows - 1)) * S::ROWB + 16 * (cx.li ^ swz(row)));
+                              (uint32_t)((prow & (uint32_t)(a.page_rows - 1)) * S::ROWB +
+                                         16 * (cx.li ^ (isv ? swz(row) : swz_k(row))));
             char* dst = sbase + (isv ? S::TK * S::ROWB : 0) + grp * 1024;
             __builtin_amdgcn_global_load_lds((const void*)src, (__attribute__((address_space(3))) void*)dst, 16, 0,
                                              kStreamAux);
@@ -179,7 +187,7 @@ __device__ __forceinline__ void issue_tile(const SplitArgs& a, const Ctx& cx, in
 #pragma unroll
         for (int i = 0; i < S::NI; ++i) {
             const int u = cx.w * S::NI + i;
-            const bool isv = u >= S::TK / 4;
+            const bool isv = wave_v;
             const int grp = isv ? u - S::TK / 4 : u;
             const int row = grp * 4 + cx.lj;
             int64_t pos;
@@ -192,7 +200,8 @@ __device__ __forceinline__ void issue_tile(const SplitArgs& a, const Ctx& cx, in
                 if (jj >= a.T) jj = a.T - 1;
                 pos = cx.n_prefix + jj;
             }
-            const char* src = (isv ? cx.vbase : cx.kbase) + pos * S::ROWB + 16 * (cx.li ^ swz(row));
+            const char* src = (isv ? cx.vbase : cx.kbase) + pos * S::ROWB +
+                              16 * (cx.li ^ (isv ? swz(row) : swz_k(row)));
             char* dst = sbase + (isv ? S::TK * S::ROWB : 0) + grp * 1024;
             __builtin_amdgcn_global_load_lds((const void*)src, (__attribute__((address_space(3))) void*)dst, 16, 0,
                                              kStreamAux);
@@ -216,13 +225,14 @@ __device__ __forceinline__ void issue_tile(const SplitArgs& a, const Ctx& cx, in
 #pragma unroll
             for (int i = 0; i < S::NI; ++i) {
                 const int u = cx.w * S::NI + i;
-                const bool isv = u >= S::TK / 4;
+                const bool isv = wave_v;
                 const int grp = isv ? u - S::TK / 4 : u;
                 const uint32_t pg = __builtin_amdgcn_readfirstlane(page[i]);
                 const char* pbase = (isv ? cx.vbase : cx.kbase) + (uint64_t)pg * (uint64_t)a.page_bytes;
                 const uint32_t r0 = (uint32_t)((k0 + grp * 4) & (a.page_rows - 1));
                 const int row = grp * 4 + cx.lj;
-                const uint32_t off = (uint32_t)(cx.lj * S::ROWB + 16 * (cx.li ^ swz(row)));
+                const uint32_t off =
+                    (uint32_t)(cx.lj * S::ROWB + 16 * (cx.li ^ (isv ? swz(row) : swz_k(row))));
                 char* dst = sbase + (isv ? S::TK * S::ROWB : 0) + grp * 1024;
                 buffer_load_lds16(raw_rsrc(pbase, head_rows_bytes), dst, off, r0 * (uint32_t)S::ROWB);
             }
@@ -254,11 +264,12 @@ __device__ __forceinline__ void issue_tile(const SplitArgs& a, const Ctx& cx, in
 #pragma unroll
         for (int i = 0; i < S::NI; ++i) {
             const int u = cx.w * S::NI + i;
-            const bool isv = u >= S::TK / 4;
+            const bool isv = wave_v;
             const int grp = isv ? u - S::TK / 4 : u;
             const int row = grp * 4 + cx.lj;
             const char* src = (isv ? cx.vbase : cx.kbase) + (uint64_t)page[i] * (uint64_t)a.page_bytes +
-                              (uint32_t)((pos[i] & (a.page_rows - 1)) * S::ROWB + 16 * (cx.li ^ swz(row)));
+                              (uint32_t)((pos[i] & (a.page_rows - 1)) * S::ROWB +
+                                         16 * (cx.li ^ row_swz(row)));
             char* dst = sbase + (isv ? S::TK * S::ROWB : 0) + grp * 1024;
             __builtin_amdgcn_global_load_lds((const void*)src, (__attribute__((address_space(3))) void*)dst, 16, 0,
                                              kStreamAux);
@@ -276,7 +287,7 @@ __device__ __forceinline__ void load_k(const char* Ks, const Ctx& cx, bf16x8 (&k
     for (int kb = 0; kb < 2; ++kb) {
         const int row = cx.ks * 32 + kb * 16 + cx.li;
         const char* base = Ks + SOFF + row * S::ROWB;
-        const int sw = swz(row);
+        const int sw = swz_k(row);
 #pragma unroll
         for (int s = 0; s < 4; ++s) kop[kb][s] = *(const bf16x8*)(base + 16 * ((4 * s + cx.lj) ^ sw));
     }
@@ -456,7 +467,7 @@ __device__ __forceinline__ void tile_pv_shared(const SplitArgs& a, const Ctx& cx
     for (int kb = 0; kb < 2; ++kb) {
         const int row = cx.ks * 32 + kb * 16 + cx.li;
         const char* base = Ks + SOFF + row * S::ROWB;
-        const int sw = swz(row);
+        const int sw = swz_k(row);
         if constexpr (S::NB <= 2) {
             // the four head-dim chunks of this 16-key half are read before
             // their products, so each product waits only for its own chunk
