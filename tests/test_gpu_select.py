@@ -165,3 +165,45 @@ def test_verify_select_repeated_calls_share_workspace():
         imp_ref = sel.importance(wl.oracle_view(q), wl.oracle_view(k), lse.cpu().numpy(), n_prefix,
                                  1 / np.sqrt(d))
         check_selection(imp_gpu, imp_ref, idx, n_prefix, 128, 4096)
+
+
+@pytest.mark.parametrize("case", range(20))
+def test_select_random_shapes(case):
+    """Seeded random shapes: tree size, head grouping (up to 32 query heads
+    per kv head, so both importance sources run: the verification kernel's
+    root scores and a pass over K), precision, committed length (tile edges
+    mixed in), kept prefix and list size; even cases the separate selection
+    call, odd cases the combined call (verification's o and lse bit for bit
+    against the plain call)."""
+    rng = np.random.default_rng(9300 + case)
+    T = int(rng.integers(1, 65))
+    G = int(rng.choice([1, 2, 3, 4, 5, 8, 16, 32]))
+    Hkv = int(rng.choice([h for h in (1, 2, 4, 8) if h * G <= 64]))
+    Hq = G * Hkv
+    dtype = "f32" if rng.random() < 0.2 else "bf16"
+    d = 128 if dtype == "bf16" else int(rng.choice([64, 128]))
+    if rng.random() < 0.3:
+        n_prefix = int(rng.choice([0, 1, 63, 64, 65, 255, 256, 257, 4095, 4096, 4097]))
+    else:
+        n_prefix = int(rng.integers(0, 20001))
+    n_keep = int(rng.choice([0, 1, 16, 64, 128, 300]))
+    n_idx = int(rng.integers(0, n_prefix + 200))
+    seed = 9300 + 17 * case
+    if case % 2 == 0:
+        run(T, Hq, Hkv, d, n_prefix, n_keep, n_idx, dtype, seed)
+        return
+    tdt = torch.float32 if dtype == "f32" else torch.bfloat16
+    q = gen((T, Hq, d), seed, tdt)
+    k = gen((Hkv, n_prefix + T, d), seed + 1, tdt)
+    v = gen((Hkv, n_prefix + T, d), seed + 2, tdt)
+    parent = wl.random_tree_parent(T, seed)
+    imp = torch.full((max(n_prefix, 1),), float("nan"), dtype=torch.float32, device="cuda")
+    say("verify_select random case %d: T=%d Hq=%d Hkv=%d d=%d n_prefix=%d keep=%d n_idx=%d %s" % (
+        case, T, Hq, Hkv, d, n_prefix, n_keep, n_idx, dtype))
+    o, lse, idx, _ = tsw.tree_attn_verify_select(q, k, v, parent, n_prefix, n_keep, n_idx, importance=imp)
+    o_ref, lse_ref = tsw.tree_attn_verify(q, k, v, parent, n_prefix)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o_ref) and torch.equal(lse, lse_ref)
+    imp_gpu = imp[:n_prefix].cpu().numpy().astype(np.float64)
+    imp_ref = sel.importance(wl.oracle_view(q), wl.oracle_view(k), lse.cpu().numpy(), n_prefix, 1 / np.sqrt(d))
+    check_selection(imp_gpu, imp_ref, idx, n_prefix, n_keep, n_idx)
