@@ -154,3 +154,56 @@ def test_penalized_acceptance_matches_oracle(T, vocab, n_recent, window, theta, 
     tsw.context_penalty(parent, lt, i32(draft), i32(recent), window, theta)
     res2 = tsw.accept_greedy(parent, lt, i32(draft)).cpu().numpy()
     assert np.array_equal(res, res2)
+
+
+@pytest.mark.parametrize("case", range(16))
+def test_penalty_random_shapes(case):
+    """Seeded random shapes: tree (random, chain, 3-ary), vocabulary size
+    (odd sizes included), window 0 .. 8192, theta (1 included), recent
+    tokens (none included), ids out of range; the in-place penalty
+    bit-exact, and the penalised acceptance equal to the oracle's acceptance
+    on the oracle's penalised logits, with the logits left unchanged."""
+    rng = np.random.default_rng(9500 + case)
+    T = int(rng.choice([1, 2, 13, 40, 64]) if rng.random() < 0.4 else rng.integers(1, 65))
+    kind = rng.integers(3)
+    parent = (wl.random_tree_parent(T, 9500 + case) if kind == 0 else
+              wl.chain_parent(T) if kind == 1 else wl.kary_tree_parent(T, 3))
+    vocab = int(rng.choice([2, 7, 1000, 5001, 32000, 128256, 151936]) if rng.random() < 0.5
+                else rng.integers(2, 200001))
+    window = int(rng.choice([0, 1, 40, 8192]) if rng.random() < 0.3 else rng.integers(0, 8193))
+    theta = float(1.0 if rng.random() < 0.15 else np.float32(rng.uniform(1.0, 3.0)))
+    n_recent = int(rng.choice([0, 1, 8]) if rng.random() < 0.2 else rng.integers(0, 10001))
+    dtype = "bf16" if rng.random() < 0.5 else "f32"
+    logits = (rng.standard_normal((T, vocab)) * 3).astype(np.float32)
+    best = logits.argmax(axis=1)
+    draft = rng.integers(0, vocab, T)
+    for i in range(1, T):
+        if rng.random() < 0.7:
+            draft[i] = best[parent[i]]
+    recent = rng.integers(0, vocab, n_recent)
+    if n_recent:
+        recent[-min(n_recent, 8):] = best[:min(n_recent, 8)] if T >= 8 else recent[-min(n_recent, 8):]
+        recent[rng.random(n_recent) < 0.01] = -3
+        recent[rng.random(n_recent) < 0.01] = vocab + 5
+    if T > 1 and rng.random() < 0.3:
+        draft[rng.integers(1, T)] = vocab
+    say("penalty random case %d: T=%d vocab=%d window=%d theta=%.4f n_recent=%d %s" % (
+        case, T, vocab, window, theta, n_recent, dtype))
+    got, want, _ = run(parent, logits, draft, recent, window, theta, dtype)
+    assert np.array_equal(got, want)
+    lt = torch.from_numpy(logits).cuda()
+    if dtype == "bf16":
+        lt = lt.to(torch.bfloat16)
+        ref_in = lt.view(torch.int16).cpu().numpy().view(np.uint16)
+    else:
+        ref_in = logits
+    before = lt.clone()
+    res = tsw.accept_greedy_penalized(parent, lt, i32(draft), i32(recent), window, theta).cpu().numpy()
+    torch.cuda.synchronize()
+    assert torch.equal(lt.view(torch.int16) if dtype == "bf16" else lt,
+                       before.view(torch.int16) if dtype == "bf16" else before)
+    path, bonus, target = acc.accept_greedy(parent, pen.penalize(ref_in, parent, draft, recent, window, theta),
+                                            draft)
+    say("  path %s bonus %d" % (list(path), bonus))
+    assert res[0] == len(path) and res[1] == bonus and list(res[2:2 + len(path)]) == list(path)
+    assert list(res[2 + T:2 + 2 * T]) == list(target)
