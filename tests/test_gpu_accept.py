@@ -164,3 +164,39 @@ def test_compact_clamps_bad_result():
     assert torch.equal(k[:, :, n_prefix + T:], k0[:, :, n_prefix + T:])
     assert torch.equal(k[0, :, n_prefix + 1], k0[0, :, n_prefix + T - 1])   # 4000 -> T-1
     assert torch.equal(k[0, :, n_prefix + 2], k0[0, :, n_prefix + 0])       # -7 -> 0
+
+
+@pytest.mark.parametrize("case", range(12))
+def test_accept_compact_random_shapes(case):
+    """Seeded random shapes for acceptance followed by compaction: tree
+    (random, chain, 3-ary) of 1-64 nodes, vocabulary, layers, kv heads, head
+    dim, precision, committed length and spare rows; drafts follow the
+    parent's argmax with a drawn probability, so paths of many lengths occur.
+    The result and every cache byte are compared with the oracle."""
+    rng = np.random.default_rng(9900 + case)
+    T = int(rng.integers(1, 65))
+    kind = rng.integers(3)
+    parent = (wl.random_tree_parent(T, 9900 + case) if kind == 0 else
+              wl.chain_parent(T) if kind == 1 else wl.kary_tree_parent(T, 3))
+    V = int(rng.choice([3, 97, 5001, 32000]))
+    layers = int(rng.integers(1, 9))
+    Hkv = int(rng.choice([1, 2, 4, 8]))
+    d = int(rng.choice([64, 128]))
+    dtype = "bf16" if rng.random() < 0.5 else "f32"
+    n_prefix = int(rng.integers(0, 3001))
+    rows = n_prefix + T + int(rng.integers(0, 11))
+    follow = float(rng.uniform(0.3, 1.0))
+    logits = rng.standard_normal((T, V)).astype(np.float32)
+    draft = np.array([0] + [P.first_max(logits[int(parent[i])]) if rng.random() < follow
+                            else int(rng.integers(0, V)) for i in range(1, T)], dtype=np.int32)
+    k, v = _caches(layers, Hkv, rows, d, dtype, 9900 + case)
+    k0, v0 = _np(k), _np(v)
+    res = tsw.accept_greedy(parent, torch.from_numpy(logits).cuda(), torch.from_numpy(draft).cuda())
+    tsw.kv_compact(k, v, n_prefix, T, res)
+    torch.cuda.synchronize()
+    path, bonus, target = acc.accept_greedy(parent, logits, draft)
+    say("accept+compact random case %d: T=%d V=%d layers=%d Hkv=%d d=%d %s n_prefix=%d path=%s" % (
+        case, T, V, layers, Hkv, d, dtype, n_prefix, list(path)))
+    check(res.cpu().numpy(), path, bonus, target, T)
+    assert np.array_equal(_np(k), acc.kv_compact(k0, n_prefix, path))
+    assert np.array_equal(_np(v), acc.kv_compact(v0, n_prefix, path))
