@@ -48,6 +48,38 @@ def test_noalloc_matches_verify_twice_then_smaller():
         assert torch.equal(o, o_ref) and torch.equal(lse, l_ref), w.name
 
 
+
+def test_noalloc_random_shapes_in_a_row():
+    """Twelve seeded random problems one after another on the shared array
+    (sizes going up and down; tree, head grouping, precision, head dim and
+    length drawn), each identical to tsw_tree_attn_verify."""
+    rng = np.random.default_rng(9800)
+    for case in range(12):
+        T = int(rng.integers(1, 65))
+        Hkv = int(rng.choice([1, 2, 4, 8]))
+        Hq = Hkv * int(rng.integers(1, 9))
+        dtype = torch.float32 if rng.random() < 0.25 else torch.bfloat16
+        d = 128 if (dtype == torch.bfloat16 and rng.random() < 0.8) else int(rng.choice([64, 128]))
+        n_prefix = int(rng.integers(0, 50001))
+        parent = wl.random_tree_parent(T, 9800 + case)
+        g = torch.Generator(device="cuda")
+        g.manual_seed(9800 + case)
+        q = torch.randn((T, Hq, d), generator=g, device="cuda").to(dtype)
+        k = torch.randn((Hkv, n_prefix + T, d), generator=g, device="cuda").to(dtype)
+        v = torch.randn((Hkv, n_prefix + T, d), generator=g, device="cuda").to(dtype)
+        need = tsw.workspace_size(q, k, n_prefix)
+        print("noalloc random case %d: T=%d Hq=%d Hkv=%d d=%d %s n_prefix=%d partials %d bytes" % (
+            case, T, Hq, Hkv, d, "bf16" if dtype == torch.bfloat16 else "f32", n_prefix, need), flush=True)
+        if need > tsw.noalloc_scratch_bytes():
+            continue
+        o_ref, l_ref = tsw.tree_attn_verify(q, k, v, parent, n_prefix)
+        o = torch.full((T, Hq, d), float("nan"), dtype=torch.float32, device="cuda")
+        lse = torch.full((T, Hq), float("nan"), dtype=torch.float32, device="cuda")
+        o, lse = tsw.tree_attn_verify_noalloc(q, k, v, parent, n_prefix, o, lse)
+        torch.cuda.synchronize()
+        assert torch.equal(o, o_ref) and torch.equal(lse, l_ref), case
+
+
 def test_noalloc_rejects_too_large():
     # 384 query rows on one kv head over a long cache (long enough that the
     # planner's floor of 3 x 384 keys per split still allows one split per
