@@ -58,7 +58,9 @@ constexpr int kStreamAux = 2;
 
 // Raw buffer resource over `bytes` bytes from `base` (stride 0, 32-bit data
 // format word): loads at offsets past the range return zeros and never
-// fault, so a ragged tile needs no clamping of its row addresses.
+// fault, so a ragged tile needs no clamping of its row addresses.  For an
+// LDS-DMA load the out-of-range dwords are written to LDS as zeros (checked
+// on gfx950), so no stale LDS contents reach the products.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_rsrc(const void* base, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }

@@ -18,8 +18,11 @@
 // eight (two per SIMD, 256 registers), each owning NB or NB-1 blocks of 16
 // query rows (R row groups) and one 32-key sub-tile of every key tile
 // (W/R sub-tiles per tile).  Per tile:
-//   * K and V rows move HBM -> LDS with global_load_lds_dwordx4 (streaming
-//     cache policy) into a 128 KB ring of two 128-key load groups: one group
+//   * K and V rows move HBM -> LDS with LDS-DMA loads (buffer loads over the
+//     split's rows of a contiguous cache and over one page's rows for whole
+//     paged prefix tiles, global loads for gathered rows and the other paged
+//     tiles; streaming cache policy; K and V rows each with their own chunk
+//     swizzle) into a 128 KB ring of two 128-key load groups: one group
 //     is in flight while the other is computed on, and one work-group
 //     barrier per group recycles its stages.
 //   * S^T = K Q^T on v_mfma_f32_16x16x32_bf16 with key rows on the M axis and
