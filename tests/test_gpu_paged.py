@@ -108,6 +108,15 @@ def test_paged_many_sequences():
     check_batch([400 + 137 * b for b in range(16)], 13, 32, 8, 16, 6)
 
 
+
+def test_paged_sixty_four_sequences():
+    """The largest batch a call takes (64 sequences: the per-sequence length
+    and split tables are full), lengths from 0 up, every row compared."""
+    rng = np.random.default_rng(64)
+    lengths = [0, 1, 63, 64, 65] + [int(x) for x in rng.integers(0, 1500, 59)]
+    check_batch(lengths, 13, 8, 2, 16, 64, parent=wl.random_tree_parent(13, 64))
+
+
 def test_paged_matches_contiguous_call():
     """One sequence in pages vs the same cache contiguous: same definition,
     two kernels; both within the tolerance of each other."""
@@ -196,6 +205,16 @@ def test_paged_partial_draft_chain_many_sequences():
     lengths = [600 + 311 * b for b in range(16)]
     check_partial_batch(lengths, [min(n, 256 + 97 * b) for b, n in enumerate(lengths)], 4, 32, 8, 16, 14,
                         parent=wl.chain_parent(4))
+
+
+
+def test_paged_partial_sixty_four_sequences():
+    """The draft pass on the largest batch: 64 sequences, lists from empty
+    to the whole cache."""
+    rng = np.random.default_rng(65)
+    lengths = [0, 1, 64, 129] + [int(x) for x in rng.integers(0, 2000, 60)]
+    n_idx = [n if b % 5 == 0 else int(rng.integers(0, n + 1)) for b, n in enumerate(lengths)]
+    check_partial_batch(lengths, n_idx, 4, 32, 8, 32, 65, parent=wl.chain_parent(4))
 
 
 def test_paged_partial_random_tree_T64():
