@@ -120,6 +120,13 @@ def test_mfma_forced_on_unsupported_shape(L):
                    parent=np.ascontiguousarray(wl.kary_tree_parent(64, 3))) == EUNSUP
 
 
+
+def test_query_rows_per_kv_head_limit(L):
+    # at most 4096 query rows (T * Hq / Hkv) share one kv head
+    par = np.ascontiguousarray(wl.kary_tree_parent(64, 3))
+    assert _verify(L, _desc(T=64, Hq=128, Hkv=1, kv_head_stride=(100 + 64) * 128), parent=par) == EUNSUP
+
+
 def test_null_pointers_and_bad_tree(L):
     d = _desc()
     assert _verify(L, d, q=None) == EINVAL

@@ -179,6 +179,14 @@ def test_valu_kernel(dtype, d, impl):
     run_case(40, 4, 4, d, 300, dtype, wl.random_tree_parent(40, 3), impl=impl, seed=d + 1)
 
 
+
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("f32", 64)])
+def test_largest_query_group(dtype, d):
+    """4096 query rows on one kv head (64 nodes x 64 query heads), the most a
+    call takes: past the matrix-core shapes, on the vector-ALU kernel."""
+    run_case(64, 64, 1, d, 700, dtype, wl.random_tree_parent(64, 31), seed=31 + d)
+
+
 def test_head_stride_padding():
     run_case(13, 8, 4, 128, 2000, "bf16", wl.kary_tree_parent(13, 3), head_pad=333, seed=5)
     run_case(13, 4, 4, 64, 500, "f32", wl.kary_tree_parent(13, 3), head_pad=17, seed=6)
