@@ -2,10 +2,11 @@
 against the float64 oracle on every (node, head) row, for shapes drawn at
 random rather than picked by hand.  Each case draws a tree (random, chain or
 3-ary), the head grouping, the head dim and precision, the committed length
-(edge values mixed in), and for the draft pass an index list, for the split
-phase an explicit split count, for the paged calls a batch of lengths and a
-page size.  Tolerances as in the other parity tests: max-abs 4e-3 for
-bfloat16 inputs, 1e-5 for float32."""
+(edge values mixed in), the kernel (bf16 cases also on the vector-ALU
+kernel), and for the draft pass an index list, for the split phase an
+explicit split count (over the whole cache or an index list), for the paged
+calls a batch of lengths and a page size.  Tolerances as in the other
+parity tests: max-abs 4e-3 for bfloat16 inputs, 1e-5 for float32."""
 import os
 import sys
 
@@ -86,6 +87,8 @@ def test_random_contiguous(case):
     n_prefix = draw_length(rng, 6000 if dtype == "bf16" else 1500)
     parent, tree = draw_tree(rng, T, seed)
     mode = rng.choice(["verify", "partial", "split"])
+    # bf16 with d = 128 also runs on the vector-ALU kernel when asked to
+    impl = str(rng.choice(["auto", "valu"])) if (dtype == "bf16" and d == 128 and rng.random() < 0.3) else "auto"
     tdt = torch.float32 if dtype == "f32" else torch.bfloat16
     cap = n_prefix + T + int(rng.integers(0, 3))
     g = torch.Generator(device="cuda")
@@ -94,21 +97,21 @@ def test_random_contiguous(case):
     k = gen((Hkv, cap, d), g, tdt)
     v = gen((Hkv, cap, d), g, tdt)
     idx = None
-    if mode == "partial":
+    if mode == "partial" or (mode == "split" and rng.random() < 0.5):
         n_idx = int(rng.integers(0, n_prefix + 1)) if rng.random() < 0.8 else n_prefix
         idx = wl.retained_index_set(n_prefix, n_idx, int(rng.choice([0, 4, 64])), seed)
-    say("case %d: %s T=%d (%s) Hq=%d Hkv=%d d=%d %s n_prefix=%d cap=%d%s" % (
-        case, mode, T, tree, Hq, Hkv, d, dtype, n_prefix, cap,
+    say("case %d: %s T=%d (%s) Hq=%d Hkv=%d d=%d %s impl=%s n_prefix=%d cap=%d%s" % (
+        case, mode, T, tree, Hq, Hkv, d, dtype, impl, n_prefix, cap,
         "" if idx is None else " n_idx=%d" % len(idx)))
+    it = None if idx is None else torch.from_numpy(idx.astype(np.int32)).cuda()
     if mode == "verify":
-        o, lse = tsw.tree_attn_verify(q, k, v, parent, n_prefix)
+        o, lse = tsw.tree_attn_verify(q, k, v, parent, n_prefix, impl=impl)
     elif mode == "partial":
-        it = torch.from_numpy(idx.astype(np.int32)).cuda()
-        o, lse = tsw.tree_attn_partial(q, k, v, parent, it, n_prefix)
+        o, lse = tsw.tree_attn_partial(q, k, v, parent, it, n_prefix, impl=impl)
     else:
         n_splits = int(rng.integers(1, 41))
         say("  n_splits=%d" % n_splits)
-        po, pl = tsw.tree_attn_split(q, k, v, parent, n_prefix, n_splits)
+        po, pl = tsw.tree_attn_split(q, k, v, parent, n_prefix, n_splits, idx=it, impl=impl)
         o, lse = tsw.lse_merge(po, pl)
     torch.cuda.synchronize()
     o_ref, lse_ref = oracle.tree_attn(wl.oracle_view(q), wl.oracle_view(k), wl.oracle_view(v), parent, n_prefix,
